@@ -1,0 +1,229 @@
+"""Seeded synthetic inputs for D = A x B + C.
+
+This module only draws random numbers and lays them out in memory; it holds
+none of the multiply-accumulate arithmetic.  Both the GPU path (tests, bench,
+smoke) and the CPU oracle consume what it produces.
+
+Storage conventions (the call contract of ``gemm_run``):
+
+* A is M x K.  Row-major: ``A(i,k) = A[i*lda + k]``, buffer shape (M, lda).
+  Col-major: ``A(i,k) = A[k*lda + i]``, buffer shape (K, lda).
+* B is K x N.  Row-major: ``B(k,j) = B[k*ldb + j]``, buffer shape (K, ldb).
+  Col-major: ``B(k,j) = B[j*ldb + k]``, buffer shape (N, ldb).
+* C and D are row-major M x N with ldc / ldd, buffer shape (M, ld).
+
+A and B hold 16-bit patterns (uint16) of fp16 or bf16; C and D hold float32
+or 16-bit patterns of the output dtype.  Padding columns of A and B (between
+the used extent and ld) are filled with NaN patterns, and D's padding with a
+sentinel, so a kernel that reads or writes outside the matrices shows up.
+
+Value recipes (the pages measure on synthetic square matrices only):
+``uniform``: U[-1,1) drawn in fp32, rounded to the input dtype (RNE);
+``normal``: N(0,1) drawn in fp32, rounded to the input dtype;
+``int``: integers in {-2,...,2} (exact in fp16/bf16).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+F32, F16, BF16 = 0, 1, 2
+ROW_MAJOR, COL_MAJOR = 0, 1
+
+NAN16 = {F16: 0x7E00, BF16: 0x7FC0}
+SENTINEL_F32 = np.float32(-12345.5)
+SENTINEL_16 = np.uint16(0x5A5A)
+
+
+def to_bits16(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float32 values to fp16/bf16 (round-to-nearest-even) -> uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == F16:
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == BF16:
+        t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16)
+        return t.numpy().view(np.uint16)
+    raise ValueError("16-bit dtype expected")
+
+
+def from_bits16(b: np.ndarray, dtype: int) -> np.ndarray:
+    """uint16 patterns -> float32 values (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    if dtype == F16:
+        return b.view(np.float16).astype(np.float32)
+    if dtype == BF16:
+        return (b.astype(np.uint32) << 16).view(np.float32)
+    raise ValueError("16-bit dtype expected")
+
+
+def _draw(rng: np.random.Generator, shape, values: str) -> np.ndarray:
+    if values == "uniform":
+        return rng.random(shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+    if values == "normal":
+        return rng.standard_normal(shape, dtype=np.float32)
+    if values == "int":
+        return rng.integers(-2, 3, size=shape).astype(np.float32)
+    if values == "zero":
+        return np.zeros(shape, dtype=np.float32)
+    raise ValueError(values)
+
+
+@dataclasses.dataclass
+class Problem:
+    """One call's worth of host-side inputs, in the gemm_run argument order."""
+    name: str
+    M: int
+    N: int
+    K: int
+    A: np.ndarray          # 2-D uint16 buffer (outer, lda)
+    lda: int
+    layoutA: int
+    B: np.ndarray          # 2-D uint16 buffer (outer, ldb)
+    ldb: int
+    layoutB: int
+    C: Optional[np.ndarray]  # 2-D buffer (M, ldc) or None
+    ldc: int
+    D: np.ndarray          # 2-D buffer (M, ldd), initialised to the sentinel (or = C)
+    ldd: int
+    in_dtype: int
+    acc_dtype: int
+    out_dtype: int
+    satf: int
+    inplace: bool = False  # C and D are the same buffer
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def _operand(rng, rows: int, cols: int, ld: int, dtype: int, values: str) -> np.ndarray:
+    """A (rows, ld) uint16 buffer whose first `cols` columns hold values, pad = NaN."""
+    buf = np.full((rows, ld), NAN16[dtype], dtype=np.uint16)
+    if rows and cols:
+        buf[:, :cols] = to_bits16(_draw(rng, (rows, cols), values), dtype)
+    return buf
+
+
+def _out_buffer(M: int, ld: int, out_dtype: int) -> np.ndarray:
+    if out_dtype == F32:
+        return np.full((M, ld), SENTINEL_F32, dtype=np.float32)
+    return np.full((M, ld), SENTINEL_16, dtype=np.uint16)
+
+
+def make_problem(M: int, N: int, K: int, *, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
+                 in_dtype=F16, acc_dtype=F32, out_dtype=F32, satf=0,
+                 values="uniform", c_values: Optional[str] = None, inplace=False,
+                 lda=None, ldb=None, ldc=None, ldd=None, seed=1234,
+                 name="custom") -> Problem:
+    """Build a seeded problem.  c_values=None means C = NULL (C = 0)."""
+    rng_a = np.random.default_rng(seed)
+    rng_b = np.random.default_rng(seed + 1)
+    rng_c = np.random.default_rng(seed + 2)
+    a_outer, a_inner = (M, K) if layoutA == ROW_MAJOR else (K, M)
+    b_outer, b_inner = (K, N) if layoutB == ROW_MAJOR else (N, K)
+    lda = max(1, a_inner) if lda is None else lda
+    ldb = max(1, b_inner) if ldb is None else ldb
+    ldd = max(1, N) if ldd is None else ldd
+    A = _operand(rng_a, a_outer, a_inner, lda, in_dtype, values)
+    B = _operand(rng_b, b_outer, b_inner, ldb, in_dtype, values)
+    C = None
+    if inplace:
+        ldc = ldd
+        D = _out_buffer(M, ldd, out_dtype)
+        if c_values is None:
+            c_values = "zero"
+        cv = _draw(rng_c, (M, N), c_values)
+        D[:, :N] = cv if out_dtype == F32 else to_bits16(cv, out_dtype)
+        C = D
+    else:
+        D = _out_buffer(M, ldd, out_dtype)
+        if c_values is not None:
+            ldc = max(1, N) if ldc is None else ldc
+            C = _out_buffer(M, ldc, out_dtype)
+            cv = _draw(rng_c, (M, N), c_values)
+            C[:, :N] = cv if out_dtype == F32 else to_bits16(cv, out_dtype)
+        else:
+            ldc = max(1, N) if ldc is None else ldc
+    return Problem(name, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                   in_dtype, acc_dtype, out_dtype, satf, inplace)
+
+
+def scale_rows(prob: Problem, frac: float, factor: float, seed: int) -> np.ndarray:
+    """Multiply round(frac*M) seeded rows of A by `factor` (a power of two, so
+    the fp16 values stay exact).  Returns the chosen row indices."""
+    rng = np.random.default_rng(seed)
+    nrows = int(round(frac * prob.M))
+    rows = np.sort(rng.choice(prob.M, size=nrows, replace=False))
+    if prob.layoutA != ROW_MAJOR:
+        raise ValueError("row scaling implemented for row-major A")
+    vals = from_bits16(prob.A[rows, :prob.K], prob.in_dtype) * np.float32(factor)
+    prob.A[rows, :prob.K] = to_bits16(vals, prob.in_dtype)
+    return rows
+
+
+def sample_indices(M: int, N: int, count: int, seed: int):
+    """Seeded (row, col) pairs, without repetition when count <= M*N."""
+    rng = np.random.default_rng(seed)
+    total = M * N
+    if count >= total:
+        flat = np.arange(total, dtype=np.int64)
+    else:
+        flat = np.sort(rng.choice(total, size=count, replace=False)).astype(np.int64)
+    return flat // N, flat % N
+
+
+# ---------------------------------------------------------------------------
+# The named workloads.  seed = 20260 + 10*index (+0 A, +1 B, +2 C; +3 scaled
+# rows; +4 output sample).
+
+def _seed(index: int) -> int:
+    return 20260 + 10 * index
+
+
+def w_256(values="uniform") -> Problem:
+    """256^3, fp16 row-major in, C = 0, fp32 out."""
+    return make_problem(256, 256, 256, values=values, seed=_seed(1),
+                        name="256^3 fp16->fp32 (%s)" % values)
+
+
+def w_4096_f16(values="uniform") -> Problem:
+    """4096^3, fp16 row-major A and B, fp32 accumulate and output, C = 0."""
+    return make_problem(4096, 4096, 4096, values=values, seed=_seed(2),
+                        name="4096^3 fp16->fp32 (%s)" % values)
+
+
+def w_4096_bf16_inplace(values="normal") -> Problem:
+    """4096^3, bf16 row-major A, bf16 col-major B, C fp32 N(0,1) updated in place."""
+    return make_problem(4096, 4096, 4096, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+                        in_dtype=BF16, values=values, c_values="normal", inplace=True,
+                        seed=_seed(3), name="4096^3 bf16 colB inplace (%s)" % values)
+
+
+def w_hgemm(satf: int, values="uniform", factor=None) -> Problem:
+    """HGEMM 3999 x 4001 x 4104, fp16 accumulate/out, padded ld, 1% of A's rows
+    scaled (x2048 uniform, x256 integer) to force overflow.  C = 0."""
+    if factor is None:
+        factor = 2048.0 if values == "uniform" else 256.0
+    p = make_problem(3999, 4001, 4104, in_dtype=F16, acc_dtype=F16, out_dtype=F16,
+                     satf=satf, values=values, c_values=None, lda=4104, ldb=4008,
+                     ldc=4008, ldd=4008, seed=_seed(4),
+                     name="HGEMM 3999x4001x4104 satf=%d (%s)" % (satf, values))
+    # C: the workload names ldc but no C values; C = 0 (explicit zero buffer)
+    p.C = np.zeros((p.M, p.ldc), dtype=np.uint16)
+    scale_rows(p, 0.01, factor, _seed(4) + 3)
+    return p
+
+
+def w_wide(values="uniform") -> Problem:
+    """16384 x 16384 x 1024, fp16 row-major in, fp32 out (sampled check)."""
+    return make_problem(16384, 16384, 1024, values=values, seed=_seed(5),
+                        name="16384x16384x1024 fp16->fp32 (%s)" % values)
+
+
+def w_skinny(values="uniform") -> Problem:
+    """16 x 16384 x 16384, fp16 row-major in, fp32 out (sampled check)."""
+    return make_problem(16, 16384, 16384, values=values, seed=_seed(6),
+                        name="16x16384x16384 fp16->fp32 (%s)" % values)

@@ -1,0 +1,176 @@
+"""CPU oracle for D = A x B + C (fp64 accumulation, one rounding to the output dtype).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` are the only callers.  The GPU library
+(``dense_mixed_precision_tiled_amd``) neither imports this package nor links its
+C code, and this package imports nothing from it.
+
+The arithmetic lives in ``gemm_oracle.c`` (plain C, built with gcc
+``-O2 -ffp-contract=off``); this module only builds it and marshals numpy
+arrays through ctypes.  Definitions followed (page title, section):
+
+* element definition, ``C[i,j] = sum_k A[i,k] * B[k,j]``:
+  "矩阵乘法优化可视化学习文档" section 1, with the triple loop of section 3;
+* ``D = A*B + C``, D in the precision of C:
+  "深入CUDA Tensor Core与WMMA…" section 2.2;
+* row/col-major addressing with a leading dimension:
+  same page sections 3.2 and 4.2;
+* in-place ``C = A*B + C`` and saturate-to-finite:
+  "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释" item (5).
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against values
+and properties the pages and the mathematics fix (no GPU involved).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gemm_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+# dtype and layout codes (the same integers the C-ABI library uses; the values
+# are part of the call contract, not shared code)
+F32, F16, BF16 = 0, 1, 2
+ROW_MAJOR, COL_MAJOR = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gemm_oracle.c into liboracle.so with gcc (host only)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-pthread", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        lib = ctypes.CDLL(LIB)
+        i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.oracle_gemm.restype = c_int
+        lib.oracle_gemm.argtypes = [i64, i64, i64, vp, i64, c_int, vp, i64, c_int,
+                                    vp, i64, vp, i64, c_int, c_int, c_int, c_int, c_int]
+        lib.oracle_gemm_sampled.restype = c_int
+        lib.oracle_gemm_sampled.argtypes = [i64, i64, i64, vp, i64, c_int, vp, i64, c_int,
+                                            vp, i64, i64, vp, vp, vp,
+                                            c_int, c_int, c_int, c_int, c_int]
+        lib.oracle_element_fp64.restype = ctypes.c_double
+        lib.oracle_element_fp64.argtypes = [i64, vp, i64, c_int, vp, i64, c_int, vp, i64,
+                                            c_int, c_int, i64, i64]
+        lib.oracle_decode_f16.restype = ctypes.c_double
+        lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        lib.oracle_decode_bf16.restype = ctypes.c_double
+        lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_round_f16.restype = ctypes.c_uint16
+        lib.oracle_round_f16.argtypes = [ctypes.c_double]
+        lib.oracle_round_bf16.restype = ctypes.c_uint16
+        lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+        lib.oracle_round_f32_bits.restype = ctypes.c_uint32
+        lib.oracle_round_f32_bits.argtypes = [ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check_in(a):
+    if a.dtype != np.uint16 or not a.flags.c_contiguous:
+        raise TypeError("A/B must be C-contiguous uint16 bit patterns")
+
+
+def _check_out(a, out_dtype):
+    want = np.float32 if out_dtype == F32 else np.uint16
+    if a.dtype != want or not a.flags.c_contiguous:
+        raise TypeError("C/D must be C-contiguous %s" % np.dtype(want).name)
+
+
+def gemm(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+         in_dtype, acc_dtype, out_dtype, satf, nthreads=None):
+    """D = A x B + C on flat buffers (numpy), same argument order as gemm_run.
+
+    A and B hold 16-bit patterns (uint16) of ``in_dtype``; C and D hold
+    ``out_dtype`` elements (float32, or uint16 patterns).  ``C`` may be None
+    (C = 0) or the same array as ``D`` with ``ldc == ldd`` (in place).  Only
+    ``D[i*ldd + j]`` with i < M, j < N is written.
+    """
+    _check_in(A)
+    _check_in(B)
+    _check_out(D, out_dtype)
+    if C is not None:
+        _check_out(C, out_dtype)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_gemm(M, N, K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                             _ptr(C), ldc, _ptr(D), ldd,
+                             in_dtype, acc_dtype, out_dtype, int(bool(satf)), nt)
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments")
+    return D
+
+
+def gemm_sampled(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, rows, cols,
+                 in_dtype, acc_dtype, out_dtype, satf, nthreads=None):
+    """Return D(rows[s], cols[s]) for every s as a dense out_dtype array."""
+    _check_in(A)
+    _check_in(B)
+    if C is not None:
+        _check_out(C, out_dtype)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    out = np.empty(rows.shape, dtype=np.float32 if out_dtype == F32 else np.uint16)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_gemm_sampled(M, N, K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                     _ptr(C), ldc, rows.size, _ptr(rows), _ptr(cols),
+                                     _ptr(out), in_dtype, acc_dtype, out_dtype,
+                                     int(bool(satf)), nt)
+    if rc != 0:
+        raise ValueError("oracle_gemm_sampled rejected its arguments")
+    return out
+
+
+def element_fp64(K, A, lda, layoutA, B, ldb, layoutB, C, ldc, in_dtype, out_dtype, i, j):
+    """The fp64 value of sum_k A(i,k)B(k,j) (+ C[i,j]) before the final rounding."""
+    return _load().oracle_element_fp64(K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                       _ptr(C), ldc, in_dtype, out_dtype, i, j)
+
+
+def decode_f16(bits: int) -> float:
+    return _load().oracle_decode_f16(bits)
+
+
+def decode_bf16(bits: int) -> float:
+    return _load().oracle_decode_bf16(bits)
+
+
+def round_f16(x: float) -> int:
+    return _load().oracle_round_f16(x)
+
+
+def round_bf16(x: float) -> int:
+    return _load().oracle_round_bf16(x)
+
+
+def round_f32_bits(x: float) -> int:
+    return _load().oracle_round_f32_bits(x)

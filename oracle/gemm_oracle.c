@@ -1,0 +1,391 @@
+/*
+ * CPU oracle for the tiled mixed-precision matrix multiply-accumulate D = A x B + C.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  The GPU library never
+ * includes, links or calls it, and this file includes nothing from the GPU
+ * library: the two share no code.
+ *
+ * What it computes (the plain definition, nothing more):
+ *   D[i,j] = round_out( sum_{k=0}^{K-1} A(i,k) * B(k,j)  +  C[i,j] ),  i < M, j < N
+ * with the sum taken in fp64, k ascending, each product and each addition
+ * rounded by plain IEEE double arithmetic (build with -ffp-contract=off so no
+ * FMA is formed), then ONE rounding (round-to-nearest-even) to the output
+ * dtype, then the saturate-to-finite rule if requested.
+ *
+ * Sources (the pages this follows):
+ *  - Element definition C[i,j] = sum over k in [0,K) of A[i,k]*B[k,j]:
+ *    "矩阵乘法优化可视化学习文档", section 1 "先建立心智模型"; the plain
+ *    triple loop in section 3 "朴素实现为什么慢".
+ *  - D = A*B + C with low-precision A, B and a high-precision C; D has the
+ *    precision of C: "深入CUDA Tensor Core与WMMA…", section 2.2
+ *    "核心运算：融合矩阵乘累加（MMA）".
+ *  - Row-major offset i*N+j and column-major offset j*M+i, generalised to a
+ *    leading dimension ld (stride between rows, resp. columns):
+ *    same page, section 3.2 (the 2x3 example) and section 4.2 (ldm);
+ *    "CUDA算子优化(5)：WMMA矩阵乘法", section "WMMA API解释" item (2).
+ *  - In-place C = A*B + C and the satf rules (+Inf -> +MAX_NORM,
+ *    -Inf -> -MAX_NORM, NaN -> +0): "CUDA算子优化(5)：WMMA矩阵乘法",
+ *    section "WMMA API解释" item (5) mma_sync.
+ *
+ * Readings where the pages are silent or disagree (each also listed in the
+ * design notes):
+ *  - acc_dtype F16 ("HGEMM": fp16 accumulator, fp16 C and D) fixes the dtype of
+ *    C, D and MAX_NORM; the value is still the exact-as-possible sum rounded
+ *    once, like every other combination.
+ *  - satf is applied once, to the final rounded output, with MAX_NORM the
+ *    largest finite value of the output dtype.
+ *  - C and D are row-major with ldc / ldd; C == NULL means C = 0.
+ *  - Rounding is IEEE round-to-nearest-even; subnormals are kept.
+ *
+ * Parity pins live in the CPU tests: exhaustive fp16 decode against numpy,
+ * the RNE encoders against numpy float16/float32 casts and an exact rational
+ * encoder, brute force of tiny GEMMs against exact rational sums, the 2x3
+ * row/col-major example, integer closed forms, the in-place invariant and the
+ * satf special cases.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_ROW_MAJOR = 0, ORACLE_COL_MAJOR = 1 };
+
+/* ---------------------------------------------------------------- decoding */
+
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_decode_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1024+m) * 2^(e-15-10) */
+    return sign ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_decode_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------- encoding */
+
+/* Round-half-to-even of a non-negative double to an integer-valued double. */
+static double rne_integer(double n)
+{
+    double fl = floor(n);
+    double frac = n - fl; /* exact: n and fl share the binade or fl == 0 */
+    if (frac > 0.5)
+        return fl + 1.0;
+    if (frac < 0.5)
+        return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/*
+ * Encode x into a binary format with p fraction bits, exponent range
+ * [emin, emax] for normal numbers, and bias = emax, rounding to nearest
+ * even.  Values whose rounded magnitude exceeds the largest finite number
+ * become infinities; tiny values become subnormals or signed zero.
+ * Returns the bit pattern (sign | exponent | fraction).
+ */
+static uint32_t rne_encode(double x, int p, int emin, int emax)
+{
+    int ebits_shift = p;
+    uint32_t sign = signbit(x) ? 1u : 0u;
+    uint32_t sign_bit = sign << (p + (emax == 15 ? 5 : 8));
+    uint32_t exp_all_ones = (emax == 15) ? 0x1fu : 0xffu;
+    if (isnan(x))
+        return sign_bit | (exp_all_ones << ebits_shift) | (1u << (p - 1));
+    double a = fabs(x);
+    if (isinf(a))
+        return sign_bit | (exp_all_ones << ebits_shift);
+    if (a == 0.0)
+        return sign_bit;
+
+    int e2;
+    frexp(a, &e2);      /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;     /* 2^e <= a < 2^(e+1) */
+    if (e < emin)
+        e = emin;       /* subnormal range: fixed quantum 2^(emin-p) */
+    double q = ldexp(1.0, e - p);     /* spacing of representable numbers */
+    double n = rne_integer(a / q);    /* a/q is exact (power-of-two scale) */
+    /* n is in [0, 2^(p+1)]; n == 2^(p+1) means carry into the next binade */
+    if (n >= ldexp(1.0, p + 1)) {
+        n = ldexp(1.0, p);
+        e += 1;
+    }
+    if (n < ldexp(1.0, p)) {
+        /* subnormal (only possible when e == emin) or zero */
+        return sign_bit | (uint32_t)n;
+    }
+    if (e > emax)
+        return sign_bit | (exp_all_ones << ebits_shift); /* overflow -> Inf */
+    uint32_t biased = (uint32_t)(e + emax);
+    uint32_t frac = (uint32_t)(n - ldexp(1.0, p));
+    return sign_bit | (biased << ebits_shift) | frac;
+}
+
+uint16_t oracle_round_f16(double x) { return (uint16_t)rne_encode(x, 10, -14, 15); }
+
+uint16_t oracle_round_bf16(double x) { return (uint16_t)rne_encode(x, 7, -126, 127); }
+
+uint32_t oracle_round_f32_bits(double x) { return rne_encode(x, 23, -126, 127); }
+
+/* -------------------------------------------------------- satf and MAX_NORM */
+
+/* Largest finite value of each output dtype, as a bit pattern. */
+static uint32_t max_norm_bits(int dtype)
+{
+    switch (dtype) {
+    case ORACLE_F16: return 0x7bffu;       /* 65504 */
+    case ORACLE_BF16: return 0x7f7fu;      /* (2 - 2^-7) * 2^127 */
+    default: return 0x7f7fffffu;           /* FLT_MAX */
+    }
+}
+
+/*
+ * Round s (fp64) to the output dtype once, then apply satf to the rounded
+ * value:  +Inf -> +MAX_NORM, -Inf -> -MAX_NORM, NaN -> +0.
+ */
+static uint32_t finish_element(double s, int out_dtype, int satf)
+{
+    uint32_t bits;
+    int is_pos_inf, is_neg_inf, is_nan;
+    if (out_dtype == ORACLE_F16) {
+        bits = oracle_round_f16(s);
+        is_nan = ((bits & 0x7c00u) == 0x7c00u) && (bits & 0x3ffu);
+        is_pos_inf = bits == 0x7c00u;
+        is_neg_inf = bits == 0xfc00u;
+    } else if (out_dtype == ORACLE_BF16) {
+        bits = oracle_round_bf16(s);
+        is_nan = ((bits & 0x7f80u) == 0x7f80u) && (bits & 0x7fu);
+        is_pos_inf = bits == 0x7f80u;
+        is_neg_inf = bits == 0xff80u;
+    } else {
+        bits = oracle_round_f32_bits(s);
+        is_nan = ((bits & 0x7f800000u) == 0x7f800000u) && (bits & 0x7fffffu);
+        is_pos_inf = bits == 0x7f800000u;
+        is_neg_inf = bits == 0xff800000u;
+    }
+    if (satf) {
+        uint32_t mx = max_norm_bits(out_dtype);
+        uint32_t sign = (out_dtype == ORACLE_F32) ? 0x80000000u : 0x8000u;
+        if (is_pos_inf)
+            bits = mx;
+        else if (is_neg_inf)
+            bits = sign | mx;
+        else if (is_nan)
+            bits = 0u;
+    }
+    return bits;
+}
+
+/* ------------------------------------------------------------ element access */
+
+static double load_in(const void *base, int dtype, int64_t off)
+{
+    uint16_t h = ((const uint16_t *)base)[off];
+    return dtype == ORACLE_BF16 ? oracle_decode_bf16(h) : oracle_decode_f16(h);
+}
+
+static double load_out(const void *base, int dtype, int64_t off)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[off];
+    uint16_t h = ((const uint16_t *)base)[off];
+    return dtype == ORACLE_BF16 ? oracle_decode_bf16(h) : oracle_decode_f16(h);
+}
+
+static void store_out(void *base, int dtype, int64_t off, uint32_t bits)
+{
+    if (dtype == ORACLE_F32)
+        ((uint32_t *)base)[off] = bits;
+    else
+        ((uint16_t *)base)[off] = (uint16_t)bits;
+}
+
+/* A(i,k): row-major -> A[i*lda + k]; col-major -> A[k*lda + i]. */
+static int64_t a_offset(int layout, int64_t lda, int64_t i, int64_t k)
+{
+    return layout == ORACLE_ROW_MAJOR ? i * lda + k : k * lda + i;
+}
+
+/* B(k,j): row-major -> B[k*ldb + j]; col-major -> B[j*ldb + k]. */
+static int64_t b_offset(int layout, int64_t ldb, int64_t k, int64_t j)
+{
+    return layout == ORACLE_ROW_MAJOR ? k * ldb + j : j * ldb + k;
+}
+
+typedef struct {
+    int64_t M, N, K;
+    const void *A; int64_t lda; int layoutA;
+    const void *B; int64_t ldb; int layoutB;
+    const void *C; int64_t ldc;
+    void *D; int64_t ldd;
+    int in_dtype, out_dtype, satf;
+    /* sampled mode */
+    int64_t nsamples;
+    const int64_t *rows, *cols;
+    void *out;
+    /* work split */
+    int64_t begin, end;
+} job_t;
+
+/* One output element, exactly the definition. */
+static double dot_plus_c(const job_t *g, int64_t i, int64_t j)
+{
+    double s = 0.0;
+    for (int64_t k = 0; k < g->K; ++k) {
+        double a = load_in(g->A, g->in_dtype, a_offset(g->layoutA, g->lda, i, k));
+        double b = load_in(g->B, g->in_dtype, b_offset(g->layoutB, g->ldb, k, j));
+        double prod = a * b;
+        s = s + prod;
+    }
+    if (g->C)
+        s = s + load_out(g->C, g->out_dtype, i * g->ldc + j);
+    return s;
+}
+
+/*
+ * Full mode, rows [begin, end).  Row i's outputs are all computed (C is read)
+ * before any of them is written, so C == D (in place) is safe.
+ */
+static void *full_worker(void *arg)
+{
+    const job_t *g = (const job_t *)arg;
+    double *row = (double *)malloc(sizeof(double) * (size_t)(g->N > 0 ? g->N : 1));
+    for (int64_t i = g->begin; i < g->end; ++i) {
+        for (int64_t j = 0; j < g->N; ++j)
+            row[j] = dot_plus_c(g, i, j);
+        for (int64_t j = 0; j < g->N; ++j)
+            store_out(g->D, g->out_dtype, i * g->ldd + j,
+                      finish_element(row[j], g->out_dtype, g->satf));
+    }
+    free(row);
+    return NULL;
+}
+
+static void *sample_worker(void *arg)
+{
+    const job_t *g = (const job_t *)arg;
+    for (int64_t s = g->begin; s < g->end; ++s) {
+        double v = dot_plus_c(g, g->rows[s], g->cols[s]);
+        store_out(g->out, g->out_dtype, s, finish_element(v, g->out_dtype, g->satf));
+    }
+    return NULL;
+}
+
+static void run_split(job_t *proto, int64_t total, int nthreads, void *(*fn)(void *))
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (total < nthreads)
+        nthreads = total > 0 ? (int)total : 1;
+    pthread_t th[256];
+    job_t jobs[256];
+    int started[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].begin = total * t / nthreads;
+        jobs[t].end = total * (t + 1) / nthreads;
+        started[t] = (nthreads > 1) && pthread_create(&th[t], NULL, fn, &jobs[t]) == 0;
+        if (!started[t])
+            fn(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t])
+            pthread_join(th[t], NULL);
+}
+
+/*
+ * Full oracle: writes D[i*ldd + j] for i < M, j < N and nothing else.
+ * A, B: 16-bit patterns of in_dtype.  C, D: elements of out_dtype (fp32 or
+ * 16-bit patterns).  acc_dtype only names the accumulator type of the call
+ * (F32, or F16 for the HGEMM variant); the value computed is the same.
+ * Returns 0, or -1 for an argument the definition does not cover.
+ */
+int oracle_gemm(int64_t M, int64_t N, int64_t K,
+                const void *A, int64_t lda, int layoutA,
+                const void *B, int64_t ldb, int layoutB,
+                const void *C, int64_t ldc,
+                void *D, int64_t ldd,
+                int in_dtype, int acc_dtype, int out_dtype, int satf, int nthreads)
+{
+    (void)acc_dtype;
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    job_t g;
+    memset(&g, 0, sizeof g);
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.layoutA = layoutA;
+    g.B = B; g.ldb = ldb; g.layoutB = layoutB;
+    g.C = C; g.ldc = ldc;
+    g.D = D; g.ldd = ldd;
+    g.in_dtype = in_dtype; g.out_dtype = out_dtype; g.satf = satf;
+    run_split(&g, M, nthreads, full_worker);
+    return 0;
+}
+
+/*
+ * Sampled oracle: out[s] = D(rows[s], cols[s]) for s < nsamples, as out_dtype
+ * elements packed densely.  Same arithmetic as oracle_gemm.
+ */
+int oracle_gemm_sampled(int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda, int layoutA,
+                        const void *B, int64_t ldb, int layoutB,
+                        const void *C, int64_t ldc,
+                        int64_t nsamples, const int64_t *rows, const int64_t *cols,
+                        void *out,
+                        int in_dtype, int acc_dtype, int out_dtype, int satf, int nthreads)
+{
+    (void)acc_dtype;
+    if (M < 0 || N < 0 || K < 0 || nsamples < 0)
+        return -1;
+    for (int64_t s = 0; s < nsamples; ++s)
+        if (rows[s] < 0 || rows[s] >= M || cols[s] < 0 || cols[s] >= N)
+            return -1;
+    job_t g;
+    memset(&g, 0, sizeof g);
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.layoutA = layoutA;
+    g.B = B; g.ldb = ldb; g.layoutB = layoutB;
+    g.C = C; g.ldc = ldc;
+    g.in_dtype = in_dtype; g.out_dtype = out_dtype; g.satf = satf;
+    g.nsamples = nsamples; g.rows = rows; g.cols = cols; g.out = out;
+    run_split(&g, nsamples, nthreads, sample_worker);
+    return 0;
+}
+
+/* Also exported for the pins: the fp64 pre-rounding value of one element. */
+double oracle_element_fp64(int64_t K,
+                           const void *A, int64_t lda, int layoutA,
+                           const void *B, int64_t ldb, int layoutB,
+                           const void *C, int64_t ldc,
+                           int in_dtype, int out_dtype, int64_t i, int64_t j)
+{
+    job_t g;
+    memset(&g, 0, sizeof g);
+    g.K = K;
+    g.A = A; g.lda = lda; g.layoutA = layoutA;
+    g.B = B; g.ldb = ldb; g.layoutB = layoutB;
+    g.C = C; g.ldc = ldc;
+    g.in_dtype = in_dtype; g.out_dtype = out_dtype;
+    return dot_plus_c(&g, i, j);
+}
