@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path: D = A x B + C through libgemm on one MI355X.
+
+Default workload: M = N = K = 4096, A and B fp16 row-major (lda = K,
+ldb = N), uniform[-1,1] (seeded), fp32 accumulate and fp32 D, C = 0.  One
+step = one gemm_run over that batch, inputs resident in HBM before the timed
+region starts.  Prints ONE JSON line:
+
+  value       = 2*M*N*K / (wall time per step) in TFLOP/s
+  roofline    = the GEMM kernel's own rate: 2*M*N*K / (mean launch duration,
+                HIP events on the launch stream) against the 2.5 PFLOP/s
+                dense fp16 MFMA peak
+  cpu_baseline= the CPU oracle on a bounded sample of the same workload (the
+                first rows of D), on this host's cores
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (2MNK/t) and % of MI355X fp16 MFMA peak, 4096³ fp16→fp32"
+PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_f16.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; counter-derived traffic is reported only when it
+    was measured on exactly these sources."""
+    csrc = os.path.join(ROOT, "dense_mixed_precision_tiled_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(prob, target_s: float):
+    """Time the oracle on the first R rows of D (all N columns, full K)."""
+    import numpy as np
+    import oracle
+
+    oracle.build(force=False)
+    threads = min(oracle.default_threads(), 16)
+
+    def run_rows(R):
+        D = np.empty((R, prob.ldd), dtype=np.float32)
+        t0 = time.perf_counter()
+        oracle.gemm(R, prob.N, prob.K, prob.A[:R].ravel(), prob.lda, prob.layoutA,
+                    prob.B.ravel(), prob.ldb, prob.layoutB, None, prob.ldc, D.ravel(),
+                    prob.ldd, prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf,
+                    nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe_rows = threads
+    t_probe = run_rows(probe_rows)
+    rows = int(max(threads, min(prob.M, probe_rows * target_s / max(t_probe, 1e-6))))
+    rows = max(threads, (rows // threads) * threads)
+    t = run_rows(rows)
+    flops = 2.0 * rows * prob.N * prob.K
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "first %d of %d rows of D (%d x %d outputs, K=%d), fp64 accumulate, "
+                  "%.1f s" % (rows, prob.M, rows, prob.N, prob.K, t),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards by output tiles with no collective; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dense_mixed_precision_tiled_amd as lg
+    from dense_mixed_precision_tiled_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lg.library()
+
+    prob = W.w_4096_f16("uniform")
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(prob.A.view(np.int16)).to(dev)
+    B = torch.from_numpy(prob.B.view(np.int16)).to(dev)
+    D = torch.empty(prob.D.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    call = (prob.M, prob.N, prob.K, A.data_ptr(), prob.lda, prob.layoutA, B.data_ptr(),
+            prob.ldb, prob.layoutB, None, prob.ldc, D.data_ptr(), prob.ldd, prob.in_dtype,
+            prob.acc_dtype, prob.out_dtype, prob.satf, stream.cuda_stream)
+    cfg = lg.gemm_select_config(prob.M, prob.N, prob.K, prob.layoutA, prob.layoutB,
+                                prob.in_dtype, prob.acc_dtype, prob.out_dtype)
+
+    for _ in range(args.warmup):
+        st = lg.gemm_run(*call)
+        if st != 0:
+            raise lg.GemmError(st)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        st = lg.gemm_run(*call)
+        ends[i].record(stream)
+        if st != 0:
+            raise lg.GemmError(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    durations_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_ms = sum(durations_ms) / len(durations_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    flop = float(prob.flops)
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (mean_ms * 1e-3) / 1e12
+    traffic = load_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "M=N=K=4096 GEMM, fp16 row-major A and B (uniform[-1,1], seeded), "
+                        "fp32 accumulate, fp32 D, C=0",
+            "M": prob.M, "N": prob.N, "K": prob.K,
+            "tile_config": lg.gemm_config_name(cfg),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "gemm_mfma_kernel<%s>" % lg.gemm_config_name(cfg),
+            "launch_ms_mean": round(mean_ms, 5),
+            "launch_ms_min": round(min(durations_ms), 5),
+            "launch_ms_median": round(sorted(durations_ms)[len(durations_ms) // 2], 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,295 @@
+// C ABI of libgemm: argument validation, the shape-class -> tile-table
+// dispatch, the split-K workspace, and the launches.  The operation and its
+// arguments are documented in include/libgemm.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/libgemm.h"
+#include "gemm_configs.hpp"
+
+using namespace libgemm;
+
+namespace libgemm {
+// Split-K reduction: D(i,j) = finish(sum over slices in slice order + C).
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(Params p) {
+    const int64_t total = (int64_t)p.M * p.N;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        float s = 0.0f;
+        for (int z = 0; z < p.splits; ++z) s += p.ws[z * total + idx];
+        finish_store(p, idx / p.N, idx % p.N, s);
+    }
+}
+
+}  // namespace libgemm
+
+namespace {
+
+struct Entry {
+    const char *name;
+    int BM, BN, BK;
+    int split_k;  // 1: this entry may split K across workgroups
+    launch_fn launch;
+};
+
+const Entry kTable[] = {
+    {"large_256x256x64_w2x2_mfma32x32x16", CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, 0,
+     launch_large},
+    {"medium_128x128x64_w2x2_mfma32x32x16", CfgMedium::BM, CfgMedium::BN, CfgMedium::BK, 0,
+     launch_medium},
+    {"small_64x64x64_w2x2_mfma32x32x16", CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, 0,
+     launch_small},
+    {"skinny_16x128x64_w1x4_mfma16x16x32_splitk", CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, 1,
+     launch_skinny},
+};
+constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
+enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3 };
+
+constexpr int kCUs = 256;  // MI355X compute units
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int out_size(int dt) { return dt == GEMM_F32 ? 4 : 2; }
+
+// Byte range [lo, hi) of a matrix with `outer` lines of `inner` elements at
+// stride ld; empty when either count is zero.
+struct Range {
+    unsigned __int128 lo, hi;
+    bool empty() const { return hi <= lo; }
+};
+
+Range extent(const void *p, int64_t outer, int64_t inner, int64_t ld, int esize) {
+    Range r;
+    r.lo = (unsigned __int128)(uintptr_t)p;
+    if (outer <= 0 || inner <= 0) {
+        r.hi = r.lo;
+        return r;
+    }
+    r.hi = r.lo + ((unsigned __int128)(outer - 1) * (unsigned __int128)ld +
+                   (unsigned __int128)inner) * (unsigned __int128)esize;
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+             const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, const void *D,
+             int64_t ldd, int in_dtype, int acc_dtype, int out_dtype) {
+    const int64_t kMaxDim = 0x7fffffff;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return GEMM_ERR_INVALID_DIM;
+    if ((layoutA != GEMM_ROW_MAJOR && layoutA != GEMM_COL_MAJOR) ||
+        (layoutB != GEMM_ROW_MAJOR && layoutB != GEMM_COL_MAJOR))
+        return GEMM_ERR_INVALID_LAYOUT;
+    if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16) return GEMM_ERR_UNSUPPORTED;
+    if (acc_dtype == GEMM_F32) {
+        if (out_dtype != GEMM_F32 && out_dtype != GEMM_F16 && out_dtype != GEMM_BF16)
+            return GEMM_ERR_UNSUPPORTED;
+    } else if (acc_dtype == GEMM_F16) {
+        if (in_dtype != GEMM_F16 || out_dtype != GEMM_F16) return GEMM_ERR_UNSUPPORTED;
+    } else {
+        return GEMM_ERR_UNSUPPORTED;
+    }
+    const int64_t a_inner = layoutA == GEMM_ROW_MAJOR ? K : M;
+    const int64_t a_outer = layoutA == GEMM_ROW_MAJOR ? M : K;
+    const int64_t b_inner = layoutB == GEMM_ROW_MAJOR ? N : K;
+    const int64_t b_outer = layoutB == GEMM_ROW_MAJOR ? K : N;
+    // leading dimensions: at least one line's worth, and small enough that
+    // every element offset fits in 62 bits
+    const int64_t kMaxLd = (int64_t)1 << 40;
+    if (lda < 1 || lda < a_inner || lda > kMaxLd) return GEMM_ERR_INVALID_LD;
+    if (ldb < 1 || ldb < b_inner || ldb > kMaxLd) return GEMM_ERR_INVALID_LD;
+    if (ldd < 1 || ldd < N || ldd > kMaxLd) return GEMM_ERR_INVALID_LD;
+    if (C && (ldc < 1 || ldc < N || ldc > kMaxLd)) return GEMM_ERR_INVALID_LD;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (!D) return GEMM_ERR_NULL_PTR;
+    if (K > 0 && (!A || !B)) return GEMM_ERR_NULL_PTR;
+
+    const int osz = out_size(out_dtype);
+    const Range rd = extent(D, M, N, ldd, osz);
+    const Range ra = K > 0 ? extent(A, a_outer, a_inner, lda, 2) : extent(A, 0, 0, 1, 2);
+    const Range rb = K > 0 ? extent(B, b_outer, b_inner, ldb, 2) : extent(B, 0, 0, 1, 2);
+    if (overlap(rd, ra) || overlap(rd, rb)) return GEMM_ERR_ALIASING;
+    if (C) {
+        const bool in_place = (C == D) && (ldc == ldd);
+        if (!in_place && overlap(extent(C, M, N, ldc, osz), rd)) return GEMM_ERR_ALIASING;
+    }
+    return GEMM_OK;
+}
+
+int select_config(int64_t M, int64_t N, int64_t K) {
+    (void)K;
+    if (M <= CfgSkinny::BM) return CFG_SKINNY;
+    const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
+    if (t_large >= 3 * kCUs / 4) return CFG_LARGE;
+    const int64_t t_medium = cdiv(M, CfgMedium::BM) * cdiv(N, CfgMedium::BN);
+    if (t_medium >= kCUs / 2) return CFG_MEDIUM;
+    return CFG_SMALL;
+}
+
+// Per (device, stream) split-K workspace, grown on demand, held until exit.
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, std::pair<float *, size_t>> g_ws;
+
+hipError_t workspace(hipStream_t stream, size_t bytes, float **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto &slot = g_ws[std::make_pair(dev, stream)];
+    if (slot.second < bytes) {
+        if (slot.first) {
+            // earlier work on this stream may still read the old buffer
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return e;
+            e = hipFree(slot.first);
+            if (e != hipSuccess) return e;
+            slot.first = nullptr;
+            slot.second = 0;
+        }
+        void *ptr = nullptr;
+        e = hipMalloc(&ptr, bytes);
+        if (e != hipSuccess) return e;
+        slot.first = static_cast<float *>(ptr);
+        slot.second = bytes;
+    }
+    *out = slot.first;
+    return hipSuccess;
+}
+
+int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+        int layoutA, const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
+        void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
+        void *stream_handle) {
+    int st = validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+                      acc_dtype, out_dtype);
+    if (st != GEMM_OK) return st;
+    if (config_id >= kNumConfigs) return GEMM_ERR_INVALID_CONFIG;
+    if (M == 0 || N == 0) return GEMM_OK;
+    const int id = config_id >= 0 ? config_id : select_config(M, N, K);
+    const Entry &E = kTable[id];
+    hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+
+    Params p;
+    p.A = static_cast<const uint16_t *>(A);
+    p.B = static_cast<const uint16_t *>(B);
+    p.C = C;
+    p.D = D;
+    p.ws = nullptr;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = C ? ldc : 0;
+    p.ldd = ldd;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.out_dtype = out_dtype;
+    p.satf = satf ? 1 : 0;
+    p.vec_ok = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % 8 == 0) &&
+               (ldb % 8 == 0);
+    p.tiles_m = (int)cdiv(M, E.BM);
+    p.tiles_n = (int)cdiv(N, E.BN);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles > 0x7fffffff) return GEMM_ERR_INVALID_DIM;
+
+    // K slices: enough workgroups for 4 per CU, each slice >= 8 K-tiles
+    int splits = 1;
+    if (E.split_k && K > 0) {
+        const int64_t want = cdiv(4 * kCUs, tiles);
+        const int64_t most = cdiv(K, (int64_t)E.BK * 8);
+        splits = (int)(want < most ? want : most);
+        if (splits < 1) splits = 1;
+    }
+    int64_t kps = cdiv(cdiv(K > 0 ? K : 1, splits), E.BK) * E.BK;
+    splits = (int)cdiv(K > 0 ? K : 1, kps);
+    p.splits = splits;
+    p.k_per_split = (int)kps;
+
+    if (splits > 1) {
+        float *ws = nullptr;
+        if (workspace(stream, (size_t)splits * (size_t)M * (size_t)N * sizeof(float), &ws) !=
+            hipSuccess)
+            return GEMM_ERR_HIP;
+        p.ws = ws;
+    }
+    const int akc = layoutA == GEMM_ROW_MAJOR;
+    const int bkc = layoutB == GEMM_COL_MAJOR;
+    dim3 grid((unsigned)tiles, 1, (unsigned)splits);
+    if (E.launch(p, in_dtype == GEMM_BF16, akc, bkc, grid, stream) != hipSuccess)
+        return GEMM_ERR_HIP;
+    if (splits > 1) {
+        const int64_t total = M * N;
+        int64_t blocks = cdiv(total, 256);
+        if (blocks > 8 * kCUs) blocks = 8 * kCUs;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+    }
+    return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+                  const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
+                  const void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype) {
+    return validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+                    acc_dtype, out_dtype);
+}
+
+int gemm_run(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+             const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, void *D,
+             int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf, void *stream) {
+    return run(-1, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype, acc_dtype,
+               out_dtype, satf, stream);
+}
+
+int gemm_run_config(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                    int layoutA, const void *B, int64_t ldb, int layoutB, const void *C,
+                    int64_t ldc, void *D, int64_t ldd, int in_dtype, int acc_dtype,
+                    int out_dtype, int satf, void *stream) {
+    if (config_id < 0 || config_id >= kNumConfigs) return GEMM_ERR_INVALID_CONFIG;
+    return run(config_id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+               acc_dtype, out_dtype, satf, stream);
+}
+
+const char *gemm_status_string(int status) {
+    switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_INVALID_DIM: return "invalid dimension (negative or above 2^31-1)";
+    case GEMM_ERR_INVALID_LD: return "leading dimension too small (or too large)";
+    case GEMM_ERR_NULL_PTR: return "null pointer for a non-empty operand";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported dtype combination";
+    case GEMM_ERR_INVALID_LAYOUT: return "layout must be GEMM_ROW_MAJOR or GEMM_COL_MAJOR";
+    case GEMM_ERR_ALIASING: return "D overlaps A or B, or C partially overlaps D";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_INVALID_CONFIG: return "no such tile-table entry";
+    default: return "unknown status";
+    }
+}
+
+int gemm_num_configs(void) { return kNumConfigs; }
+
+const char *gemm_config_name(int config_id) {
+    if (config_id < 0 || config_id >= kNumConfigs) return nullptr;
+    return kTable[config_id].name;
+}
+
+int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB, int in_dtype,
+                       int acc_dtype, int out_dtype) {
+    // validate everything that does not involve pointers or leading dims
+    const int st = validate(M, N, K, nullptr, 1 + (layoutA == GEMM_ROW_MAJOR ? K : M), layoutA,
+                            nullptr, 1 + (layoutB == GEMM_ROW_MAJOR ? N : K), layoutB, nullptr,
+                            1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype);
+    if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
+    return select_config(M, N, K);
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// The tile-shape table: one TileCfg per entry, and the launcher each kernel
+// translation unit defines for it.
+#pragma once
+
+#include "gemm_kernels.hpp"
+
+namespace libgemm {
+
+// Large square-ish problems: 256x256 block tile, 2x2 waves of 128x128
+// (4x4 MFMA 32x32x16 tiles per wave), BK 64, two LDS stages = 128 KiB.
+using CfgLarge = TileCfg<256, 256, 64, 2, 2, 32, 4>;
+// Mid-size problems: 128x128, 2x2 waves of 64x64.
+using CfgMedium = TileCfg<128, 128, 64, 2, 2, 32, 4>;
+// Small problems: 64x64, 2x2 waves of 32x32.
+using CfgSmall = TileCfg<64, 64, 64, 2, 2, 32, 4>;
+// Skinny M <= 16: 16x128 tile, 1x4 waves of 16x32 with the 16x16x32 MFMA,
+// split-K so enough workgroups stream B.
+using CfgSkinny = TileCfg<16, 128, 64, 1, 4, 16, 1>;
+
+typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
+                                dim3 grid, hipStream_t stream);
+
+hipError_t launch_large(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_medium(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_small(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_skinny(const Params &, int, int, int, dim3, hipStream_t);
+
+template <class CF, bool BF, bool AKC, bool BKC>
+hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC>), grid, dim3(CF::THREADS), 0, s, p);
+    return hipGetLastError();
+}
+
+template <class CF, bool BF>
+hipError_t launch_layouts(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
+    if (akc)
+        return bkc ? launch_one<CF, BF, true, true>(p, grid, s)
+                   : launch_one<CF, BF, true, false>(p, grid, s);
+    return bkc ? launch_one<CF, BF, false, true>(p, grid, s)
+               : launch_one<CF, BF, false, false>(p, grid, s);
+}
+
+template <class CF>
+hipError_t launch_cfg(const Params &p, int bf, int akc, int bkc, dim3 grid, hipStream_t s) {
+    return bf ? launch_layouts<CF, true>(p, akc, bkc, grid, s)
+              : launch_layouts<CF, false>(p, akc, bkc, grid, s);
+}
+
+}  // namespace libgemm

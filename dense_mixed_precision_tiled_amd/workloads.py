@@ -93,6 +93,7 @@ class Problem:
     out_dtype: int
     satf: int
     inplace: bool = False  # C and D are the same buffer
+    extra: dict = dataclasses.field(default_factory=dict)  # recipe details (e.g. scaled rows)
 
     @property
     def flops(self) -> int:
@@ -213,7 +214,7 @@ def w_hgemm(satf: int, values="uniform", factor=None) -> Problem:
                      name="HGEMM 3999x4001x4104 satf=%d (%s)" % (satf, values))
     # C: the workload names ldc but no C values; C = 0 (explicit zero buffer)
     p.C = np.zeros((p.M, p.ldc), dtype=np.uint16)
-    scale_rows(p, 0.01, factor, _seed(4) + 3)
+    p.extra["scaled_rows"] = scale_rows(p, 0.01, factor, _seed(4) + 3)
     return p
 
 

@@ -1,0 +1,164 @@
+/*
+ * libgemm — tiled mixed-precision matrix multiply-accumulate D = A x B + C
+ * on AMD Instinct MI355X (gfx950), as hand-written HIP kernels behind a C ABI.
+ *
+ * The operation (sources, by page title and section):
+ *  - D = A*B + C, fused multiply-accumulate with low-precision A, B and a
+ *    high-precision accumulator; D has the precision of C:
+ *    "深入CUDA Tensor Core与WMMA：从基础原理到高性能混合精度矩阵乘实战",
+ *    section 2.2 "核心运算：融合矩阵乘累加（MMA）".
+ *  - Element definition C[i,j] = sum over k in [0,K) of A[i,k]*B[k,j]:
+ *    "矩阵乘法优化可视化学习文档", section 1 "先建立心智模型".
+ *  - Row-major / column-major storage with a leading dimension (stride, in
+ *    elements, between consecutive rows resp. columns): "深入CUDA Tensor Core
+ *    与WMMA…", sections 3.2 (2x3 example) and 4.2 (ldm); "CUDA算子优化(5)：
+ *    WMMA矩阵乘法", section "WMMA API解释" items (2) and (3).
+ *  - In-place C = A*B + C, and satf (saturate to finite): +Inf -> +MAX_NORM,
+ *    -Inf -> -MAX_NORM, NaN -> +0: "CUDA算子优化(5)：WMMA矩阵乘法",
+ *    section "WMMA API解释" item (5) mma_sync.
+ *  - fp16-accumulate HGEMM variant (fp16 A, B, C, D):
+ *    "hgemm_mma_m16n8k16_naive_kernel", section 1.1 "m16n8k16 指令规格".
+ *
+ * Readings where the pages leave a step open:
+ *  - C and D are row-major (C(i,j) = C[i*ldc + j]); C has the output dtype.
+ *  - acc_dtype GEMM_F16 selects the HGEMM variant: C, D and MAX_NORM are fp16.
+ *    The sum itself is accumulated in fp32 (gfx950's f16 MFMAs accumulate in
+ *    fp32) and rounded once to fp16, the accuracy the page on mixed precision
+ *    asks for (section 7.1 "常见坑点", item 5).
+ *  - satf is applied once, to the value rounded to out_dtype; MAX_NORM is the
+ *    largest finite value of out_dtype.
+ *  - Rounding to fp16 / bf16 is round-to-nearest-even.
+ *  - Nothing outside rows [0,M) and columns [0,N) of D is written, and no
+ *    element of A or B outside the M x K and K x N matrices is read.
+ */
+#ifndef LIBGEMM_H
+#define LIBGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage order of A and B. */
+typedef enum {
+    GEMM_ROW_MAJOR = 0, /* X(r,c) = X[r*ld + c] */
+    GEMM_COL_MAJOR = 1  /* X(r,c) = X[c*ld + r] */
+} gemm_layout_t;
+
+/* Element types. */
+typedef enum {
+    GEMM_F32 = 0,  /* IEEE binary32 */
+    GEMM_F16 = 1,  /* IEEE binary16 */
+    GEMM_BF16 = 2  /* bfloat16 (upper half of binary32) */
+} gemm_dtype_t;
+
+/* Return codes.  GEMM_OK means "validated and enqueued". */
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_DIM = -1,    /* M, N or K negative, or above 2^31-1        */
+    GEMM_ERR_INVALID_LD = -2,     /* a leading dimension shorter than its matrix */
+    GEMM_ERR_NULL_PTR = -3,       /* NULL A, B or D for a non-empty operation    */
+    GEMM_ERR_UNSUPPORTED = -4,    /* dtype combination not provided              */
+    GEMM_ERR_INVALID_LAYOUT = -5, /* layout not GEMM_ROW_MAJOR / GEMM_COL_MAJOR  */
+    GEMM_ERR_ALIASING = -6,       /* D overlaps A or B, or C partially overlaps D */
+    GEMM_ERR_HIP = -7,            /* the HIP runtime reported an error           */
+    GEMM_ERR_INVALID_CONFIG = -8  /* gemm_run_config: no such config, or the
+                                     config cannot run this problem            */
+} gemm_status_t;
+
+/*
+ * D = A x B + C on the device.
+ *
+ *   M, N, K      problem size: A is M x K, B is K x N, C and D are M x N.
+ *                M == 0 or N == 0: nothing to do, returns GEMM_OK.
+ *                K == 0: D = satf(round(C)) (or +0 when C is NULL).
+ *   A, lda, layoutA   device pointer to in_dtype elements; lda >= K when
+ *                row-major, >= M when col-major (and >= 1).
+ *   B, ldb, layoutB   device pointer to in_dtype elements; ldb >= N when
+ *                row-major, >= K when col-major (and >= 1).
+ *   C, ldc       device pointer to out_dtype elements, row-major, ldc >= N;
+ *                may be NULL (C = 0).  C == D with ldc == ldd is the in-place
+ *                update C = A x B + C; any other overlap of C and D is rejected.
+ *   D, ldd       device pointer to out_dtype elements, row-major, ldd >= N.
+ *   in_dtype     GEMM_F16 or GEMM_BF16.
+ *   acc_dtype    GEMM_F32 (out_dtype F32, F16 or BF16), or GEMM_F16 with
+ *                in_dtype == out_dtype == GEMM_F16 (HGEMM).
+ *   out_dtype    dtype of C and D.
+ *   satf         nonzero: +Inf -> +MAX_NORM, -Inf -> -MAX_NORM, NaN -> +0.
+ *   stream       a hipStream_t (NULL = the null stream).  The work is enqueued
+ *                on it; the call does not wait for it.
+ *
+ * Ownership: every pointer is owned by the caller and must stay valid until
+ * the stream reaches the enqueued work.  The library keeps one internal
+ * device workspace per device for split-K partial sums (allocated on first
+ * need, grown on demand with hipMalloc, freed at unload); calls that overlap
+ * on one device from different host threads are serialised around it.
+ *
+ * Errors: argument errors are detected on the host before anything is
+ * enqueued, and nothing is written.  GEMM_ERR_HIP reports a launch or
+ * allocation failure; faults inside the kernels surface at the next
+ * synchronisation of the stream.
+ *
+ * Speed: 16-byte vector loads are used where A and B base pointers are
+ * 16-byte aligned and lda, ldb are multiples of 8 elements (the pages' ldm
+ * rule); any other alignment runs correct element-wise loads.
+ */
+int gemm_run(int64_t M, int64_t N, int64_t K,
+             const void *A, int64_t lda, int layoutA,
+             const void *B, int64_t ldb, int layoutB,
+             const void *C, int64_t ldc,
+             void *D, int64_t ldd,
+             int in_dtype, int acc_dtype, int out_dtype,
+             int satf, void *stream);
+
+/* Static text for a gemm_status_t value ("unknown status" otherwise). */
+const char *gemm_status_string(int status);
+
+/*
+ * The tile-shape table.  Each entry is one tiling (block tile, wave grid,
+ * MFMA shape, split-K policy); the dispatcher of gemm_run picks an entry per
+ * shape class.  Tiling and autotuning by shape: "矩阵乘法优化可视化学习文档",
+ * section 6 "常用优化方法总表" (Tiling, Autotuning rows).
+ *
+ * gemm_num_configs: number of entries.
+ * gemm_config_name: static text naming entry `config_id` (NULL if out of range).
+ * gemm_select_config: the entry gemm_run would use for this problem, or a
+ *                negative gemm_status_t if the arguments are invalid.
+ */
+int gemm_num_configs(void);
+const char *gemm_config_name(int config_id);
+int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB,
+                       int in_dtype, int acc_dtype, int out_dtype);
+
+/*
+ * gemm_run with the tile-table entry forced to `config_id` (same arguments,
+ * same validation, same results up to summation order).  For tests and
+ * benchmarks that must reach every entry.  GEMM_ERR_INVALID_CONFIG if the
+ * entry does not exist.
+ */
+int gemm_run_config(int config_id,
+                    int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda, int layoutA,
+                    const void *B, int64_t ldb, int layoutB,
+                    const void *C, int64_t ldc,
+                    void *D, int64_t ldd,
+                    int in_dtype, int acc_dtype, int out_dtype,
+                    int satf, void *stream);
+
+/*
+ * Host-only argument check of gemm_run (no HIP call, no device needed):
+ * returns GEMM_OK or the error gemm_run would return before enqueuing.
+ */
+int gemm_validate(int64_t M, int64_t N, int64_t K,
+                  const void *A, int64_t lda, int layoutA,
+                  const void *B, int64_t ldb, int layoutB,
+                  const void *C, int64_t ldc,
+                  const void *D, int64_t ldd,
+                  int in_dtype, int acc_dtype, int out_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_H */

@@ -1,0 +1,178 @@
+"""Helpers for the GPU parity tests: move a seeded Problem to the device, run
+it through the C ABI, and compare with the CPU oracle to the stated bar.
+
+Tolerances (written here, derived in the design notes):
+  fp32 out : per element |err| <= 1e-4*sqrt(K), relative Frobenius <= 1e-5
+  fp16 out : per element |err| <= 2^-10*|ref| + 2e-3*sqrt(K); where the exact
+             value lies within that bound of the fp16 overflow threshold 65520,
+             +-65504 and +-Inf of the same sign are both accepted
+  bf16 out : per element |err| <= 2^-7*|ref| + 1e-4*sqrt(K) (one bf16 ulp from
+             rounding an fp32 sum instead of the exact one, plus the fp32 bound)
+  integer-valued inputs: bit-exact (IEEE equality; NaN positions equal)
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import dense_mixed_precision_tiled_amd as lg
+import oracle
+from dense_mixed_precision_tiled_amd.workloads import (BF16, F16, F32, SENTINEL_16,
+                                                       SENTINEL_F32, from_bits16)
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16 if x.dtype == np.uint16
+                                                      else x.dtype))
+    return t.to("cuda")
+
+
+def _host(t: torch.Tensor, like: np.ndarray) -> np.ndarray:
+    return t.cpu().numpy().view(like.dtype).reshape(like.shape)
+
+
+class DeviceProblem:
+    """Device copies of a Problem's buffers (C aliases D when in place)."""
+
+    def __init__(self, prob):
+        self.prob = prob
+        self.A = _dev(prob.A)
+        self.B = _dev(prob.B)
+        self.D = _dev(prob.D)
+        if prob.inplace:
+            self.C = self.D
+        elif prob.C is not None:
+            self.C = _dev(prob.C)
+        else:
+            self.C = None
+
+    def reset_D(self):
+        self.D.copy_(_dev(self.prob.D))
+
+    def run(self, config=None, stream=None, satf=None):
+        p = self.prob
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        args = (p.M, p.N, p.K, self.A.data_ptr(), p.lda, p.layoutA, self.B.data_ptr(), p.ldb,
+                p.layoutB, None if self.C is None else self.C.data_ptr(), p.ldc,
+                self.D.data_ptr(), p.ldd, p.in_dtype, p.acc_dtype, p.out_dtype,
+                p.satf if satf is None else satf, s)
+        st = lg.gemm_run(*args) if config is None else lg.gemm_run_config(config, *args)
+        if st != 0:
+            raise lg.GemmError(st)
+        return st
+
+    def result(self) -> np.ndarray:
+        torch.cuda.synchronize()
+        return _host(self.D, self.prob.D)
+
+    def gather(self, rows, cols) -> np.ndarray:
+        """D(rows[s], cols[s]) copied back, gathered on the device."""
+        torch.cuda.synchronize()
+        p = self.prob
+        flat = torch.from_numpy(np.asarray(rows, np.int64) * p.ldd + np.asarray(cols, np.int64))
+        vals = self.D.reshape(-1)[flat.to("cuda")].cpu().numpy()
+        return vals.view(p.D.dtype)
+
+
+def oracle_full(prob) -> np.ndarray:
+    """The oracle's D buffer (full M x N region; padding keeps the sentinel)."""
+    D = prob.D.copy()
+    C = D if prob.inplace else prob.C
+    oracle.gemm(prob.M, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                prob.B.ravel(), prob.ldb, prob.layoutB,
+                None if C is None else C.ravel(), prob.ldc, D.ravel(), prob.ldd,
+                prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf)
+    return D
+
+
+def oracle_samples(prob, rows, cols) -> np.ndarray:
+    C = prob.D if prob.inplace else prob.C  # prob.D still holds the original C
+    return oracle.gemm_sampled(prob.M, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                               prob.B.ravel(), prob.ldb, prob.layoutB,
+                               None if C is None else C.ravel(), prob.ldc, rows, cols,
+                               prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf)
+
+
+def values(x: np.ndarray, out_dtype: int) -> np.ndarray:
+    if out_dtype == F32:
+        return x.astype(np.float64)
+    return from_bits16(x, out_dtype).astype(np.float64)
+
+
+def compare(prob, got, ref, exact: bool, rows=None, cols=None, label=""):
+    """got/ref: out_dtype element arrays of equal shape (region or samples).
+    Raises AssertionError with the first offending elements."""
+    K = prob.K
+    g = values(np.asarray(got), prob.out_dtype).ravel()
+    r = values(np.asarray(ref), prob.out_dtype).ravel()
+    nan_g, nan_r = np.isnan(g), np.isnan(r)
+    assert np.array_equal(nan_g, nan_r), "%s: NaN positions differ (%d vs %d)" % (
+        label, nan_g.sum(), nan_r.sum())
+    ok = ~nan_r
+    g, r = g[ok], r[ok]
+    if exact:
+        bad = np.nonzero(g != r)[0]
+        assert bad.size == 0, "%s: %d of %d not bit-exact, e.g. got %s ref %s" % (
+            label, bad.size, g.size, g[bad[:5]], r[bad[:5]])
+        return
+    root = math.sqrt(max(K, 0))
+    if prob.out_dtype == F32:
+        bound = np.full_like(r, 1e-4 * root)
+    elif prob.out_dtype == F16:
+        bound = 2.0 ** -10 * np.abs(r) + 2e-3 * root
+    else:
+        bound = 2.0 ** -7 * np.abs(r) + 1e-4 * root
+    inf_g, inf_r = np.isinf(g), np.isinf(r)
+    fin = ~inf_g & ~inf_r
+    err = np.abs(g[fin] - r[fin])
+    badf = np.nonzero(err > bound[fin])[0]
+    # overflow classification near the fp16 threshold
+    special = np.nonzero(inf_g | inf_r)[0]
+    bad_special = []
+    if special.size:
+        idx = np.nonzero(ok)[0][special]
+        for s_i, flat in zip(special, idx):
+            gv, rv = g[s_i], r[s_i]
+            if gv == rv:
+                continue
+            if prob.out_dtype == F16 and np.sign(gv) == np.sign(rv) and \
+                    abs(gv) >= 65504 and abs(rv) >= 65504:
+                i, j = (rows[flat], cols[flat]) if rows is not None else divmod(flat, prob.N)
+                C = prob.D if prob.inplace else prob.C
+                s = oracle.element_fp64(prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                                        prob.B.ravel(), prob.ldb, prob.layoutB,
+                                        None if C is None else C.ravel(), prob.ldc,
+                                        prob.in_dtype, prob.out_dtype, int(i), int(j))
+                band = 2.0 ** -10 * 65520 + 2e-3 * root
+                if abs(abs(s) - 65520.0) <= band:
+                    continue
+            bad_special.append((gv, rv))
+    assert badf.size == 0, "%s: %d of %d beyond tolerance, e.g. got %s ref %s bound %s" % (
+        label, badf.size, err.size, g[fin][badf[:5]], r[fin][badf[:5]], bound[fin][badf[:5]])
+    assert not bad_special, "%s: Inf mismatch %s" % (label, bad_special[:5])
+    if prob.out_dtype == F32 and fin.any():
+        nr = np.linalg.norm(r[fin])
+        if nr > 0:
+            rel = np.linalg.norm(g[fin] - r[fin]) / nr
+            assert rel <= 1e-5, "%s: relative Frobenius error %.3g > 1e-5" % (label, rel)
+
+
+def region(prob, D: np.ndarray) -> np.ndarray:
+    return D[:prob.M, :prob.N]
+
+
+def check_padding(prob, D: np.ndarray, label=""):
+    """Columns N..ldd-1 of D still hold the sentinel (in place: C's padding)."""
+    if prob.ldd > prob.N:
+        pad = D[:prob.M, prob.N:]
+        want = prob.D[:prob.M, prob.N:]
+        assert np.array_equal(pad.view(np.uint8), want.view(np.uint8)), \
+            "%s: D padding was written" % label

@@ -1,0 +1,127 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_mixed_precision_tiled_amd as lg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgemm.h")
+
+R, Cm = lg.GEMM_ROW_MAJOR, lg.GEMM_COL_MAJOR
+F32, F16, BF16 = lg.GEMM_F32, lg.GEMM_F16, lg.GEMM_BF16
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lg.LIB_PATH):
+        from dense_mixed_precision_tiled_amd import build
+        build.build()
+    return lg.library()
+
+
+def test_header_declares_the_calls():
+    assert _declared_functions() == sorted(lg.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(-8, 1):
+        s = lg.gemm_status_string(code)
+        assert s and s != "unknown status", code
+    assert lg.gemm_status_string(-99) == "unknown status"
+
+
+def test_config_table(lib):
+    n = lg.gemm_num_configs()
+    assert n >= 4
+    names = [lg.gemm_config_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert lg.gemm_config_name(n) is None and lg.gemm_config_name(-1) is None
+
+
+def test_dispatcher_shape_classes(lib):
+    names = {i: lg.gemm_config_name(i) for i in range(lg.gemm_num_configs())}
+    pick = lambda M, N, K: names[lg.gemm_select_config(M, N, K, R, R, F16, F32, F32)]
+    assert pick(4096, 4096, 4096).startswith("large")
+    assert pick(3999, 4001, 4104).startswith("large")
+    assert pick(16384, 16384, 1024).startswith("large")
+    assert pick(16, 16384, 16384).startswith("skinny")
+    assert pick(256, 256, 256).startswith("small")
+    assert lg.gemm_select_config(-1, 4, 4, R, R, F16, F32, F32) == -1
+    assert lg.gemm_select_config(4, 4, 4, 7, R, F16, F32, F32) == -5
+    assert lg.gemm_select_config(4, 4, 4, R, R, F32, F32, F32) == -4
+
+
+# fake, distinct, 16-byte aligned addresses: gemm_validate never dereferences
+A0, B0, C0, D0 = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def v(M=8, N=8, K=8, A=A0, lda=None, la=R, B=B0, ldb=None, lb=R, C=None, ldc=None, D=D0,
+      ldd=None, i=F16, a=F32, o=F32):
+    lda = max(1, K if la == R else M) if lda is None else lda
+    ldb = max(1, N if lb == R else K) if ldb is None else ldb
+    ldd = max(1, N) if ldd is None else ldd
+    ldc = max(1, N) if ldc is None else ldc
+    return lg.gemm_validate(M, N, K, A, lda, la, B, ldb, lb, C, ldc, D, ldd, i, a, o)
+
+
+def test_validation_ok_cases(lib):
+    assert v() == 0
+    assert v(la=Cm, lb=Cm) == 0
+    assert v(C=C0) == 0
+    assert v(C=D0) == 0                      # in place, ldc == ldd
+    assert v(i=BF16, o=BF16) == 0
+    assert v(i=F16, a=F16, o=F16) == 0       # HGEMM
+    assert v(M=0, A=None, B=None, D=None) == 0
+    assert v(N=0, A=None, B=None, D=None) == 0
+    assert v(K=0, A=None, B=None, lda=1, ldb=8) == 0   # K = 0: A, B unused
+    assert v(lda=13, ldb=9, ldd=11) == 0     # padded (unaligned) leading dims
+
+
+def test_validation_errors(lib):
+    assert v(M=-1) == -1 and v(N=-1) == -1 and v(K=-1) == -1
+    assert v(M=2 ** 31) == -1
+    assert v(lda=7) == -2 and v(ldb=7) == -2 and v(ldd=7) == -2
+    assert v(C=C0, ldc=7) == -2
+    assert v(la=Cm, lda=7) == -2 and v(lb=Cm, ldb=7) == -2
+    assert v(M=0, lda=0) == -2               # ld >= 1 always
+    assert v(A=None) == -3 and v(B=None) == -3 and v(D=None) == -3
+    assert v(i=F32) == -4 and v(a=BF16) == -4
+    assert v(i=BF16, a=F16, o=F16) == -4 and v(a=F16, o=F32) == -4
+    assert v(la=2) == -5 and v(lb=-1) == -5
+    assert v(D=A0 + 64) == -6                # D inside A
+    assert v(D=B0) == -6
+    assert v(C=D0 + 4) == -6                 # C partially overlaps D
+    assert v(C=D0, ldc=9, ldd=8) == -6       # same base, different ld
+
+
+def test_run_rejects_before_touching_the_device(lib):
+    # argument errors return before any HIP call, so this works without a GPU
+    st = lg.gemm_run(-1, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0, None)
+    assert st == -1
+    st = lg.gemm_run_config(99, 8, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0,
+                            None)
+    assert st == -8
+    st = lg.gemm_run(0, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0, None)
+    assert st == 0  # empty problem: nothing enqueued
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(lg, "_lib", None)
+    monkeypatch.setattr(lg, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        lg.library()

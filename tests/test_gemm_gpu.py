@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes are compared element by element over the whole output; the
+full-size workloads on seeded samples of 65,536 outputs (plus properties of
+the whole output).  Integer-valued inputs must be bit-exact; random inputs
+meet the tolerances stated in gpu_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_mixed_precision_tiled_amd as lg
+from dense_mixed_precision_tiled_amd import workloads as W
+from dense_mixed_precision_tiled_amd.workloads import BF16, COL_MAJOR, F16, F32, ROW_MAJOR
+from gpu_util import (DeviceProblem, check_padding, compare, log, oracle_full,
+                      oracle_samples, region)
+
+pytestmark = pytest.mark.gpu
+
+NSAMPLE = 65536
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    lg.library()  # raises if the HIP library is missing: no fallback
+    torch.cuda.init()
+    yield
+
+
+def _full_check(prob, exact, config=None, label=None):
+    label = label or prob.name
+    log("case: %s config=%s" % (label, config))
+    dp = DeviceProblem(prob)
+    dp.run(config=config)
+    got = dp.result()
+    ref = oracle_full(prob)
+    compare(prob, region(prob, got), region(prob, ref), exact, label=label)
+    check_padding(prob, got, label)
+    return got
+
+
+def _sampled_check(prob, exact, seed, extra_rows=None, label=None):
+    label = label or prob.name
+    log("case: %s (sampled)" % label)
+    dp = DeviceProblem(prob)
+    dp.run()
+    rows, cols = W.sample_indices(prob.M, prob.N, NSAMPLE, seed)
+    if extra_rows is not None:
+        er = np.repeat(np.asarray(extra_rows, np.int64), prob.N)
+        ec = np.tile(np.arange(prob.N, dtype=np.int64), len(extra_rows))
+        rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+    got = dp.gather(rows, cols)
+    ref = oracle_samples(prob, rows, cols)
+    compare(prob, got, ref, exact, rows=rows, cols=cols, label=label)
+    return dp
+
+
+# ------------------------------------------------------------ the workloads
+
+@pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
+def test_256_cube(values, exact):
+    _full_check(W.w_256(values), exact)
+
+
+@pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
+def test_4096_fp16_to_fp32(values, exact):
+    prob = W.w_4096_f16(values)
+    dp = _sampled_check(prob, exact, seed=20264)
+    # whole-output properties: finite, and row/column sums match the fp64
+    # sums of A*(B 1) and (1^T A)*B within N (resp. M) per-element bounds
+    D = dp.result().astype(np.float64)
+    assert np.isfinite(D).all()
+    a = W.from_bits16(prob.A, F16).astype(np.float64)
+    b = W.from_bits16(prob.B, F16).astype(np.float64)
+    tol = 1e-4 * np.sqrt(prob.K)
+    rows_ref = a @ b.sum(axis=1)
+    cols_ref = a.sum(axis=0) @ b
+    slack = 0.0 if exact else 1.0
+    assert np.max(np.abs(D.sum(axis=1) - rows_ref)) <= prob.N * tol * slack + 1e-6 * np.abs(rows_ref).max()
+    assert np.max(np.abs(D.sum(axis=0) - cols_ref)) <= prob.M * tol * slack + 1e-6 * np.abs(cols_ref).max()
+
+
+@pytest.mark.parametrize("values,exact", [("normal", False), ("int", True)])
+def test_4096_bf16_colB_inplace(values, exact):
+    # integer variant: integer A and B, C normal(0,1); fl32(S + C) with S exact
+    # equals the oracle's single rounding of S + C
+    prob = W.w_4096_bf16_inplace(values)
+    _sampled_check(prob, exact, seed=20274)
+
+
+@pytest.mark.parametrize("satf", [0, 1])
+@pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
+def test_hgemm_ragged_overflow(satf, values, exact):
+    prob = W.w_hgemm(satf, values)
+    scaled = prob.extra["scaled_rows"]
+    assert len(scaled) == 40
+    dp = _sampled_check(prob, exact, seed=20284, extra_rows=scaled[:6])
+    D = dp.result()
+    check_padding(prob, D, prob.name)
+    v = W.from_bits16(D[:prob.M, :prob.N], F16)
+    if satf:
+        assert np.isfinite(v).all(), "satf left a non-finite value"
+    else:
+        assert np.isinf(v).any(), "the scaled rows should overflow fp16"
+
+
+@pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
+def test_wide_16384x16384x1024(values, exact):
+    _sampled_check(W.w_wide(values), exact, seed=20294)
+
+
+@pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
+def test_skinny_16x16384x16384(values, exact):
+    _sampled_check(W.w_skinny(values), exact, seed=20304)
+
+
+# ------------------------------------------------- every tile-table entry
+
+def _entry_shapes():
+    out = []
+    for cid in range(4):
+        if cid == 3:
+            out.append((cid, 13, 3 * 128 - 5, 1100))
+        else:
+            bm = (256, 128, 64)[cid]
+            out.append((cid, 2 * bm + 17, 3 * bm - 5, 200))
+    return out
+
+
+@pytest.mark.parametrize("cid,M,N,K", _entry_shapes())
+def test_every_entry_layouts_dtypes(cid, M, N, K):
+    for in_dt in (F16, BF16):
+        for la in (ROW_MAJOR, COL_MAJOR):
+            for lb in (ROW_MAJOR, COL_MAJOR):
+                for values, exact in (("int", True), ("uniform", False)):
+                    prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, in_dtype=in_dt,
+                                          values=values, seed=1000 + cid)
+                    _full_check(prob, exact, config=cid,
+                                label="cfg%d %dx%dx%d in=%d A%d B%d %s" % (
+                                    cid, M, N, K, in_dt, la, lb, values))
+
+
+@pytest.mark.parametrize("cid,M,N,K", _entry_shapes())
+def test_every_entry_output_modes(cid, M, N, K):
+    modes = [
+        dict(out_dtype=F16, acc_dtype=F16, c_values="uniform", ldd=N + 3, satf=1),
+        dict(out_dtype=BF16, acc_dtype=F32, c_values="normal", ldd=N + 8),
+        dict(out_dtype=F32, acc_dtype=F32, c_values="normal", inplace=True, ldd=N + 5),
+        dict(out_dtype=F32, acc_dtype=F32, c_values=None, lda=None, ldd=N + 1),
+    ]
+    for mode in modes:
+        for values, exact in (("int", True), ("uniform", False)):
+            cv = mode.get("c_values")
+            if values == "int" and cv is not None:
+                mode = dict(mode, c_values="int")
+            prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+                                  in_dtype=F16, values=values, seed=2000 + cid, **mode)
+            _full_check(prob, exact, config=cid,
+                        label="cfg%d out=%d acc=%d inplace=%s %s" % (
+                            cid, prob.out_dtype, prob.acc_dtype, prob.inplace, values))
+
+
+@pytest.mark.parametrize("cid", range(4))
+def test_unaligned_leading_dims(cid):
+    # lda, ldb not multiples of 8 elements: the element-wise load path
+    M, N, K = (37, 45, 77) if cid != 3 else (9, 300, 700)
+    for la, lb in ((ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR)):
+        a_in = K if la == ROW_MAJOR else M
+        b_in = N if lb == ROW_MAJOR else K
+        prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, values="int",
+                              lda=a_in + 1, ldb=b_in + 3, ldd=N + 2, c_values="int",
+                              seed=3000 + cid)
+        _full_check(prob, True, config=cid, label="cfg%d unaligned A%d B%d" % (cid, la, lb))
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 7, 3), (5, 1, 9), (17, 33, 8), (31, 15, 9),
+                                   (64, 64, 64), (65, 63, 65), (16, 16, 1), (33, 257, 31),
+                                   (100, 100, 0)])
+def test_small_and_degenerate_shapes(shape):
+    M, N, K = shape
+    for values, exact in (("int", True), ("uniform", False)):
+        prob = W.make_problem(M, N, K, values=values, c_values="int" if exact else "normal",
+                              ldd=N + 1, seed=4000 + M + N + K)
+        _full_check(prob, exact, label="%dx%dx%d %s" % (M, N, K, values))
+
+
+def test_empty_problem_writes_nothing():
+    prob = W.make_problem(0, 8, 8, ldd=8)
+    dp = DeviceProblem(prob)
+    dp.run()
+    prob2 = W.make_problem(8, 0, 8, ldd=1)
+    dp2 = DeviceProblem(prob2)
+    dp2.run()
+    assert np.array_equal(dp2.result().view(np.uint8), prob2.D.view(np.uint8))
+
+
+@pytest.mark.parametrize("out_dt", [F32, F16, BF16])
+def test_satf_special_values_on_gpu(out_dt):
+    """C = +Inf, -Inf, NaN with finite A*B -> +MAX_NORM, -MAX_NORM, +0 under
+    satf; unchanged specials without it."""
+    M, N, K = 40, 70, 33
+    acc = F16 if out_dt == F16 else F32
+    for satf in (0, 1):
+        prob = W.make_problem(M, N, K, in_dtype=F16, acc_dtype=acc, out_dtype=out_dt,
+                              values="int", c_values="int", satf=satf, seed=5000)
+        specials = np.array([np.inf, -np.inf, np.nan], dtype=np.float32)
+        C = W.from_bits16(prob.C, out_dt) if out_dt != F32 else prob.C.copy()
+        C[::3, :N] = specials[0]
+        C[1::3, :N] = specials[1]
+        C[2::7, :N] = specials[2]
+        prob.C = C if out_dt == F32 else W.to_bits16(C, out_dt)
+        got = _full_check(prob, True, label="satf=%d out=%d" % (satf, out_dt))
+        v = W.from_bits16(region(prob, got), out_dt) if out_dt != F32 else region(prob, got)
+        if satf:
+            assert np.isfinite(v).all()
+        else:
+            assert np.isinf(v).any() and np.isnan(v).any()
+
+
+def test_golden_2x3_example_on_gpu():
+    """The pages' 2x3 matrix stored col-major as A, times I3: D row-major is
+    1,2,3,4,5,6 (the row-major order printed on the page)."""
+    A = np.array([1, 4, 2, 5, 3, 6], dtype=np.float16).view(np.uint16).reshape(3, 2)
+    B = np.eye(3, dtype=np.float16).view(np.uint16)
+    prob = W.make_problem(2, 3, 3, layoutA=COL_MAJOR, values="zero", seed=1)
+    prob.A = A.copy()
+    prob.lda = 2
+    prob.B = B.copy()
+    dp = DeviceProblem(prob)
+    dp.run()
+    got = dp.result()
+    assert list(got[:2, :3].ravel()) == [1, 2, 3, 4, 5, 6]
+
+
+def test_nondefault_stream_and_determinism():
+    prob = W.make_problem(300, 500, 700, values="uniform", seed=6000)
+    dp = DeviceProblem(prob)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dp.run(stream=s)
+    s.synchronize()
+    first = dp.result().copy()
+    ref = oracle_full(prob)
+    compare(prob, region(prob, first), region(prob, ref), False, label="side stream")
+    for _ in range(3):
+        dp.reset_D()
+        dp.run()
+        again = dp.result()
+        assert np.array_equal(first.view(np.uint8), again.view(np.uint8)), "nondeterministic"
