@@ -50,6 +50,22 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Keeps
+// every accumulator index a constant so the accumulators stay in registers.
+template <int B, int E>
+struct Unroll {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&f) {
+        f(std::integral_constant<int, B>{});
+        Unroll<B + 1, E>::run(f);
+    }
+};
+template <int E>
+struct Unroll<E, E> {
+    template <class F>
+    __device__ __forceinline__ static void run(F &&) {}
+};
+
 // Everything a launch needs; passed by value as the kernel argument.
 struct Params {
     const uint16_t *A;
@@ -310,35 +326,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     return (uint16_t)(u >> 16);
 }
 
-// v = acc (+ C), rounded once to out_dtype, then satf, stored at D(i,j).
-__device__ __forceinline__ void finish_store(const Params &p, int64_t i, int64_t j, float v) {
+// v = acc (+ C), rounded once to the output dtype OUT, then satf, stored at
+// D(i,j).  OUT is a template argument so the hot epilogue has no dtype branch.
+template <int OUT>
+__device__ __forceinline__ void finish_store_t(const Params &p, int64_t i, int64_t j, float v) {
     if (p.C) v += load_c(p, i, j);
     const int64_t off = i * p.ldd + j;
-    if (p.out_dtype == DT_F32) {
+    if constexpr (OUT == DT_F32) {
         if (p.satf) {
             if (__builtin_isnan(v)) v = 0.0f;
             else if (__builtin_isinf(v)) v = v > 0 ? 3.402823466e38f : -3.402823466e38f;
         }
         reinterpret_cast<float *>(p.D)[off] = v;
     } else {
+        constexpr uint16_t expo = (OUT == DT_F16) ? 0x7c00u : 0x7f80u;
+        constexpr uint16_t mx = (OUT == DT_F16) ? 0x7bffu : 0x7f7fu;
         uint16_t h;
-        uint16_t mx;
-        if (p.out_dtype == DT_F16) {
+        if constexpr (OUT == DT_F16)
             h = __builtin_bit_cast(uint16_t, (_Float16)v);
-            mx = 0x7bffu;
-        } else {
+        else
             h = f32_to_bf16_rne(v);
-            mx = 0x7f7fu;
-        }
-        if (p.satf) {
-            const uint16_t expo = (p.out_dtype == DT_F16) ? 0x7c00u : 0x7f80u;
-            if ((h & expo) == expo) {
-                if (h & (uint16_t)(~expo & 0x7fffu)) h = 0;        // NaN -> +0
-                else h = (uint16_t)((h & 0x8000u) | mx);         // +-Inf -> +-MAX_NORM
-            }
+        if (p.satf && (h & expo) == expo) {
+            if (h & (uint16_t)(~expo & 0x7fffu)) h = 0;          // NaN -> +0
+            else h = (uint16_t)((h & 0x8000u) | mx);           // +-Inf -> +-MAX_NORM
         }
         reinterpret_cast<uint16_t *>(p.D)[off] = h;
     }
+}
+
+__device__ __forceinline__ void finish_store(const Params &p, int64_t i, int64_t j, float v) {
+    if (p.out_dtype == DT_F32) finish_store_t<DT_F32>(p, i, j, v);
+    else if (p.out_dtype == DT_F16) finish_store_t<DT_F16>(p, i, j, v);
+    else finish_store_t<DT_BF16>(p, i, j, v);
 }
 
 // ------------------------------------------------------------ tile mapping
@@ -392,12 +411,11 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     LA la;
     LB lb;
     Acc acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < AccT<MF>::N; ++r) acc[i][j][r] = 0.0f;
+    Unroll<0, TM>::run([&](auto ii) {
+        Unroll<0, TN>::run([&](auto jj) {
+            acc[decltype(ii)::value][decltype(jj)::value] = Acc{};
+        });
+    });
 
     auto load_tiles = [&](int kt) {
         const int k0 = kbeg + kt * BK;
@@ -437,15 +455,15 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                 const int r = wn * CF::WTN + j * MF + (lane & (MF - 1));
                 bf[j] = b_s[r * CH + (chunk ^ swz(r))];
             }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
+            Unroll<0, TM>::run([&](auto ii) {
+                Unroll<0, TN>::run([&](auto jj) {
+                    constexpr int i = decltype(ii)::value, j = decltype(jj)::value;
                     if constexpr (MF == 32)
                         acc[i][j] = mfma32<BF>(af[i], bf[j], acc[i][j]);
                     else
                         acc[i][j] = mfma16<BF>(af[i], bf[j], acc[i][j]);
-                }
+                });
+            });
         }
 
         if (kt + 1 < nk) {
@@ -455,22 +473,44 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         __syncthreads();
     }
 
-    // Epilogue: split-K slices store raw fp32 partial sums; otherwise finish.
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < AccT<MF>::N; ++r) {
-                const int gi = m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane, r);
-                const int gj = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane);
-                if (gi < p.M && gj < p.N) {
-                    if (p.splits > 1)
-                        p.ws[((int64_t)blockIdx.z * p.M + gi) * p.N + gj] = acc[i][j][r];
-                    else
-                        finish_store(p, gi, gj, acc[i][j][r]);
-                }
-            }
+    // Epilogue: split-K slices store raw fp32 partial sums (OUT = -1);
+    // otherwise C add, convert, satf and store.  Interior tiles skip the
+    // bounds checks.
+    const bool full_tile = (m0 + BM <= p.M) && (n0 + BN <= p.N);
+    auto epilogue = [&](auto out_tag, auto check_tag) {
+        constexpr int OUT = decltype(out_tag)::value;
+        constexpr bool CHECK = decltype(check_tag)::value;
+        Unroll<0, TM>::run([&](auto ii) {
+            Unroll<0, TN>::run([&](auto jj) {
+                Unroll<0, AccT<MF>::N>::run([&](auto rr) {
+                    constexpr int i = decltype(ii)::value, j = decltype(jj)::value;
+                    constexpr int r = decltype(rr)::value;
+                    const int gi = m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane, r);
+                    const int gj = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane);
+                    if (!CHECK || (gi < p.M && gj < p.N)) {
+                        if constexpr (OUT < 0)
+                            p.ws[((int64_t)blockIdx.z * p.M + gi) * p.N + gj] = acc[i][j][r];
+                        else
+                            finish_store_t<OUT>(p, gi, gj, acc[i][j][r]);
+                    }
+                });
+            });
+        });
+    };
+    using IC_T = std::integral_constant<bool, true>;
+    using IC_F = std::integral_constant<bool, false>;
+    if (p.splits > 1) {
+        epilogue(std::integral_constant<int, -1>{}, IC_T{});
+    } else if (p.out_dtype == DT_F32) {
+        if (full_tile) epilogue(std::integral_constant<int, DT_F32>{}, IC_F{});
+        else epilogue(std::integral_constant<int, DT_F32>{}, IC_T{});
+    } else if (p.out_dtype == DT_F16) {
+        if (full_tile) epilogue(std::integral_constant<int, DT_F16>{}, IC_F{});
+        else epilogue(std::integral_constant<int, DT_F16>{}, IC_T{});
+    } else {
+        if (full_tile) epilogue(std::integral_constant<int, DT_BF16>{}, IC_F{});
+        else epilogue(std::integral_constant<int, DT_BF16>{}, IC_T{});
+    }
 }
 
 }  // namespace libgemm
