@@ -43,7 +43,7 @@ const Entry kTable[] = {
      launch_medium},
     {"small_64x64x64_w2x2_mfma32x32x16", CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, 0,
      launch_small},
-    {"skinny_16x128x64_w1x4_mfma16x16x32_splitk", CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, 1,
+    {"skinny_16x128x128_w1x4_mfma16x16x32_splitk", CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, 1,
      launch_skinny},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
@@ -191,8 +191,19 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     p.K = (int)K;
     p.out_dtype = out_dtype;
     p.satf = satf ? 1 : 0;
-    p.vec_ok = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && (lda % 8 == 0) &&
-               (ldb % 8 == 0);
+    // Vector path: 16-byte aligned operands whose extents (rounded up to 16
+    // bytes) fit a 32-bit buffer range
+    const int64_t a_ext = (layoutA == GEMM_ROW_MAJOR ? (M - 1) * lda + K : (K - 1) * lda + M) * 2;
+    const int64_t b_ext = (layoutB == GEMM_ROW_MAJOR ? (K - 1) * ldb + N : (N - 1) * ldb + K) * 2;
+    const int64_t a_rng = (a_ext + 15) & ~(int64_t)15, b_rng = (b_ext + 15) & ~(int64_t)15;
+    p.vec_ok = K > 0 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
+               (lda % 8 == 0) && (ldb % 8 == 0) && a_rng < ((int64_t)1 << 32) - 16 &&
+               b_rng < ((int64_t)1 << 32) - 16;
+    p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
+    p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
+    const int osz = out_dtype == GEMM_F32 ? 4 : 2;
+    p.cd_vec = ((uintptr_t)D % (4 * osz) == 0) && (ldd % 4 == 0) &&
+               (!C || (((uintptr_t)C % (4 * osz) == 0) && (ldc % 4 == 0)));
     p.tiles_m = (int)cdiv(M, E.BM);
     p.tiles_n = (int)cdiv(N, E.BN);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;

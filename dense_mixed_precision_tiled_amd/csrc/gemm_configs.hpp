@@ -13,9 +13,9 @@ using CfgLarge = TileCfg<256, 256, 64, 2, 2, 32, 4>;
 using CfgMedium = TileCfg<128, 128, 64, 2, 2, 32, 4>;
 // Small problems: 64x64, 2x2 waves of 32x32.
 using CfgSmall = TileCfg<64, 64, 64, 2, 2, 32, 4>;
-// Skinny M <= 16: 16x128 tile, 1x4 waves of 16x32 with the 16x16x32 MFMA,
-// split-K so enough workgroups stream B.
-using CfgSkinny = TileCfg<16, 128, 64, 1, 4, 16, 1>;
+// Skinny M <= 16: 16x128x128 tile, 1x4 waves of 16x32 with the 16x16x32
+// MFMA, split-K so enough workgroups stream B.
+using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16, 1>;
 
 typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
                                 dim3 grid, hipStream_t stream);
@@ -27,7 +27,17 @@ hipError_t launch_skinny(const Params &, int, int, int, dim3, hipStream_t);
 
 template <class CF, bool BF, bool AKC, bool BKC>
 hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC>), grid, dim3(CF::THREADS), 0, s, p);
+    // the K loop masks k >= kend only when some slice ends inside a K-tile
+    const bool ragged = (p.K % CF::BK) != 0 || (p.k_per_split % CF::BK) != 0;
+    if (!p.vec_ok)
+        hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC, false, false>), grid,
+                           dim3(CF::THREADS), 0, s, p);
+    else if (ragged)
+        hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC, true, true>), grid,
+                           dim3(CF::THREADS), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC, true, false>), grid,
+                           dim3(CF::THREADS), 0, s, p);
     return hipGetLastError();
 }
 

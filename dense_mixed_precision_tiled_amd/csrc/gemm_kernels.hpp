@@ -78,6 +78,8 @@ struct Params {
     int out_dtype;
     int satf;
     int vec_ok;      // A, B 16-byte aligned with lda, ldb multiples of 8
+    int cd_vec;      // C, D rows allow 4-element vector access (aligned base, ld % 4 == 0)
+    uint32_t a_bytes, b_bytes;  // vector path: A, B extents rounded up to 16 bytes
     int tiles_m, tiles_n;
     int splits;      // K slices (blockIdx.z); 1 = no split
     int k_per_split; // multiple of BK
@@ -119,12 +121,48 @@ __device__ __forceinline__ uint32_t half_of(const u32x4 &v, int e) {
     return (e & 1) ? hi16(d) : lo16(d);
 }
 
+// {element e of a, element e of b} packed into one dword (low half from a),
+// for a and b holding 8 16-bit values each: one v_perm_b32 (byte select from
+// the pair {b, a}, a supplying bytes 0-3).
+__device__ __forceinline__ uint32_t pair_of(const u32x4 &a, const u32x4 &b, int e) {
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], sel);
+}
+
 // ---------------------------------------------------------------- loaders
 // Operand X with "rows" r (M for A, N for B) and depth k.
 //  K-contiguous storage: X(r,k) = X[r*ld + k]   (row-major A, col-major B)
 //  R-contiguous storage: X(r,k) = X[k*ld + r]   (col-major A, row-major B)
-// Each loader fetches one ROWS x BK tile into registers (load_*) and writes
-// it to LDS K-contiguous (store).
+// Each loader fetches one ROWS x BK tile into registers and writes it to LDS
+// K-contiguous (store).
+//
+// Vector path (16-byte aligned operands, extent < 4 GiB): 16-byte buffer
+// loads through a descriptor whose range is the operand's extent rounded up
+// to 16 bytes, so every read past the end returns zeros.  Per-lane offsets
+// are fixed for the K loop; the K position goes in the scalar offset.  Rows
+// beyond R are clamped to the last valid row (8-row chunk): they only feed
+// outputs that are never stored.  k >= kend must read as zero; with RAGGED
+// the loaded values are masked (only a ragged last K-tile has any such k).
+// Threads beyond a small tile's chunk count duplicate a chunk (same value to
+// the same LDS address), which keeps the code free of branches.
+//
+// Checked path (unaligned operands): element-wise loads with zero fill.
+
+// Keep the first n (0..8) 16-bit elements of a 16-byte chunk, zero the rest.
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t m = (2 * q + 1 < n) ? 0xffffffffu : (2 * q < n ? 0x0000ffffu : 0u);
+        v[q] &= m;
+    }
+    return v;
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                            uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff,
+                                                                            (int)soff, 0));
+}
 
 template <int ROWS, int BK, int THREADS>
 struct LoaderKC {
@@ -132,46 +170,69 @@ struct LoaderKC {
     static constexpr int TOTAL = ROWS * CH;  // 16-byte chunks in the tile
     static constexpr bool PARTIAL = TOTAL < THREADS;
     static constexpr int PER = PARTIAL ? 1 : TOTAL / THREADS;
+    static constexpr int NLOAD = PER, NSTORE = PER;
     static_assert(PARTIAL || TOTAL % THREADS == 0, "tile/threads");
+    static_assert(PARTIAL || THREADS % CH == 0, "threads/chunks");
     u32x4 v[PER];
+    uint32_t voff[PER];  // byte offset of each chunk at k = 0
+    int kc;              // this thread's k offset inside the K-tile
 
-    __device__ __forceinline__ void load_fast(const uint16_t *X, int64_t ld, int r0, int k0,
-                                              int tid) {
+    __device__ __forceinline__ static int chunk(int i, int tid) {
+        return PARTIAL ? tid % TOTAL : i * THREADS + tid;
+    }
+
+    __device__ __forceinline__ void init(int tid, int64_t ld, int r0, int R) {
+        kc = (chunk(0, tid) % CH) * 8;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = i * THREADS + tid;
-            if (PARTIAL && q >= TOTAL) break;
-            const int r = q / CH, c = q % CH;
-            v[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)(r0 + r) * ld + (k0 + c * 8));
+            const int r = min(r0 + chunk(i, tid) / CH, R - 1);
+            voff[i] = (uint32_t)(((int64_t)r * ld + kc) * 2);
         }
     }
 
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = buf_load16(rsrc, voff[i], (uint32_t)k0 * 2u);
+    }
+
+    // the idx-th global load / LDS store of load() / store(), one instruction
+    template <int idx>
+    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t) {
+        v[idx] = buf_load16(rsrc, voff[idx], (uint32_t)k0 * 2u);
+    }
+    template <int idx>
+    __device__ __forceinline__ void store_one(u32x4 *lds, int tid) const {
+        const int q = chunk(idx, tid);
+        const int r = q / CH, c = q % CH;
+        lds[r * CH + (c ^ swz(r))] = v[idx];
+    }
+
+    __device__ __forceinline__ void mask(int k0, int kend) {
+        const int n = min(max(kend - (k0 + kc), 0), 8);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = keep_first(v[i], n);
+    }
+
     __device__ __forceinline__ void load_checked(const uint16_t *X, int64_t ld, int r0, int k0,
-                                                 int R, int Kend, int vec_ok, int tid) {
+                                                 int R, int Kend, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = i * THREADS + tid;
-            if (PARTIAL && q >= TOTAL) break;
+            const int q = chunk(i, tid);
             const int r = q / CH, c = q % CH;
             const int gr = r0 + r, gk = k0 + c * 8;
-            if (gr < R && gk + 8 <= Kend && vec_ok) {
-                v[i] = *reinterpret_cast<const u32x4 *>(X + (int64_t)gr * ld + gk);
-            } else {
-                uint32_t h[8];
+            uint32_t h[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    h[e] = (gr < R && gk + e < Kend) ? (uint32_t)X[(int64_t)gr * ld + gk + e] : 0u;
-                v[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                             h[6] | (h[7] << 16)};
-            }
+            for (int e = 0; e < 8; ++e)
+                h[e] = (gr < R && gk + e < Kend) ? (uint32_t)X[(int64_t)gr * ld + gk + e] : 0u;
+            v[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16)};
         }
     }
 
     __device__ __forceinline__ void store(u32x4 *lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int q = i * THREADS + tid;
-            if (PARTIAL && q >= TOTAL) break;
+            const int q = chunk(i, tid);
             const int r = q / CH, c = q % CH;
             lds[r * CH + (c ^ swz(r))] = v[i];
         }
@@ -187,50 +248,103 @@ struct LoaderRC {
     static constexpr int KB = PERT < 8 ? PERT : 8;   // k-depth of one block
     static constexpr int NBLK = PERT / KB;           // blocks per thread
     static constexpr int NBLOCKS = TOTAL / KB;       // blocks in the tile
+    static constexpr int NLOAD = NBLK * KB, NSTORE = NBLK * 8;
     static_assert(PARTIAL || TOTAL % THREADS == 0, "tile/threads");
     static_assert(KB == 1 || KB == 2 || KB == 4 || KB == 8, "k-depth");
     static_assert(PERT % KB == 0, "blocks");
     static_assert(BK % KB == 0, "k groups");
-    u32x4 v[NBLK][KB];  // v[j][kk]: 8 consecutive r at k = kg*KB + kk
+    static_assert(PARTIAL || THREADS % RCH == 0, "threads/row chunks");
+    u32x4 v[NBLK][KB];  // v[j][kk]: 8 consecutive r at k = kg_j*KB + kk
+    uint32_t voff;      // byte offset of this thread's 8-row chunk at k = 0
+    int kg[NBLK];       // k-group of each block
 
     // block b -> (kg, rb): rb fastest, so adjacent lanes read adjacent 16 B
-    __device__ __forceinline__ void load_fast(const uint16_t *X, int64_t ld, int r0, int k0,
-                                              int tid) {
+    __device__ __forceinline__ static int block(int j, int tid) {
+        return PARTIAL ? tid % NBLOCKS : j * THREADS + tid;
+    }
+
+    __device__ __forceinline__ void init(int tid, int64_t ld, int r0, int R) {
+        const int rb = block(0, tid) % RCH;   // the same for every j
+        const int col = min(r0 + rb * 8, (R - 1) & ~7);
+        voff = (uint32_t)(col * 2);
 #pragma unroll
-        for (int j = 0; j < NBLK; ++j) {
-            const int b = j * THREADS + tid;
-            if (PARTIAL && b >= NBLOCKS) break;
-            const int rb = b % RCH, kg = b / RCH;
-            const uint16_t *src = X + (int64_t)(k0 + kg * KB) * ld + (r0 + rb * 8);
+        for (int j = 0; j < NBLK; ++j) kg[j] = block(j, tid) / RCH;
+    }
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld) {
+        const uint32_t ldb = (uint32_t)ld * 2u;
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j)
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk)
-                v[j][kk] = *reinterpret_cast<const u32x4 *>(src + (int64_t)kk * ld);
-        }
+                v[j][kk] = buf_load16(rsrc, voff + (uint32_t)(kg[j] * KB + kk) * ldb,
+                                      (uint32_t)k0 * ldb);
+    }
+
+    template <int idx>
+    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld) {
+        constexpr int j = idx / KB, kk = idx % KB;
+        const uint32_t ldb = (uint32_t)ld * 2u;
+        v[j][kk] = buf_load16(rsrc, voff + (uint32_t)(kg[j] * KB + kk) * ldb, (uint32_t)k0 * ldb);
+    }
+
+    __device__ __forceinline__ void mask(int k0, int kend) {
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk)
+                if (k0 + kg[j] * KB + kk >= kend) v[j][kk] = u32x4{0u, 0u, 0u, 0u};
     }
 
     __device__ __forceinline__ void load_checked(const uint16_t *X, int64_t ld, int r0, int k0,
-                                                 int R, int Kend, int vec_ok, int tid) {
+                                                 int R, int Kend, int tid) {
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
-            const int b = j * THREADS + tid;
-            if (PARTIAL && b >= NBLOCKS) break;
-            const int rb = b % RCH, kg = b / RCH;
+            const int b = block(j, tid);
+            const int rb = b % RCH, kgb = b / RCH;
             const int gr = r0 + rb * 8;
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) {
-                const int gk = k0 + kg * KB + kk;
+                const int gk = k0 + kgb * KB + kk;
                 const uint16_t *src = X + (int64_t)gk * ld + gr;
-                if (gk < Kend && gr + 8 <= R && vec_ok) {
-                    v[j][kk] = *reinterpret_cast<const u32x4 *>(src);
-                } else {
-                    uint32_t h[8];
+                uint32_t h[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        h[e] = (gk < Kend && gr + e < R) ? (uint32_t)src[e] : 0u;
-                    v[j][kk] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                     h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-                }
+                for (int e = 0; e < 8; ++e)
+                    h[e] = (gk < Kend && gr + e < R) ? (uint32_t)src[e] : 0u;
+                v[j][kk] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                 h[6] | (h[7] << 16)};
             }
+        }
+    }
+
+    // the idx-th LDS store of store(): block idx / 8, column idx % 8
+    template <int idx>
+    __device__ __forceinline__ void store_one(u32x4 *lds, int tid) const {
+        store_col(lds, tid, idx / 8, idx % 8);
+    }
+
+    __device__ __forceinline__ void store_col(u32x4 *lds, int tid, int j, int e) const {
+        constexpr int CH = BK / 8;
+        const int b = block(j, tid);
+        const int rb = b % RCH, kgb = b / RCH;
+        const int kofs = kgb * KB;
+        const int c = kofs / 8, sub = kofs % 8;  // chunk and element offset
+        const int r = rb * 8 + e;
+        u32x4 *dst = lds + r * CH + (c ^ swz(r));
+        if constexpr (KB == 8) {
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = pair_of(v[j][2 * q], v[j][2 * q + 1], e);
+            *dst = w;
+        } else if constexpr (KB == 4) {
+            u32x2 w;
+            w[0] = pair_of(v[j][0], v[j][1], e);
+            w[1] = pair_of(v[j][2], v[j][3], e);
+            reinterpret_cast<u32x2 *>(dst)[sub / 4] = w;
+        } else if constexpr (KB == 2) {
+            reinterpret_cast<uint32_t *>(dst)[sub / 2] = pair_of(v[j][0], v[j][1], e);
+        } else {
+            reinterpret_cast<uint16_t *>(dst)[sub] = (uint16_t)half_of(v[j][0], e);
         }
     }
 
@@ -240,10 +354,9 @@ struct LoaderRC {
         constexpr int CH = BK / 8;
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
-            const int b = j * THREADS + tid;
-            if (PARTIAL && b >= NBLOCKS) break;
-            const int rb = b % RCH, kg = b / RCH;
-            const int kofs = kg * KB;
+            const int b = block(j, tid);
+            const int rb = b % RCH, kgb = b / RCH;
+            const int kofs = kgb * KB;
             const int c = kofs / 8, sub = kofs % 8;  // chunk and element offset
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -252,17 +365,15 @@ struct LoaderRC {
                 if constexpr (KB == 8) {
                     u32x4 w;
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        w[p] = half_of(v[j][2 * p], e) | (half_of(v[j][2 * p + 1], e) << 16);
+                    for (int q = 0; q < 4; ++q) w[q] = pair_of(v[j][2 * q], v[j][2 * q + 1], e);
                     *dst = w;
                 } else if constexpr (KB == 4) {
                     u32x2 w;
-                    w[0] = half_of(v[j][0], e) | (half_of(v[j][1], e) << 16);
-                    w[1] = half_of(v[j][2], e) | (half_of(v[j][3], e) << 16);
+                    w[0] = pair_of(v[j][0], v[j][1], e);
+                    w[1] = pair_of(v[j][2], v[j][3], e);
                     reinterpret_cast<u32x2 *>(dst)[sub / 4] = w;
                 } else if constexpr (KB == 2) {
-                    reinterpret_cast<uint32_t *>(dst)[sub / 2] =
-                        half_of(v[j][0], e) | (half_of(v[j][1], e) << 16);
+                    reinterpret_cast<uint32_t *>(dst)[sub / 2] = pair_of(v[j][0], v[j][1], e);
                 } else {
                     reinterpret_cast<uint16_t *>(dst)[sub] = (uint16_t)half_of(v[j][0], e);
                 }
@@ -360,6 +471,85 @@ __device__ __forceinline__ void finish_store(const Params &p, int64_t i, int64_t
     else finish_store_t<DT_BF16>(p, i, j, v);
 }
 
+// Four consecutive outputs D(i, j..j+3) from fp32 sums v: split-K slices
+// store the raw sums; otherwise C is added, the result rounded once to the
+// output dtype, satf applied, and the group stored with one vector store
+// when it is whole and aligned.  Outputs outside M x N are skipped.
+__device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) {
+    const int nval = min(p.N - j, 4);
+    if (i >= p.M || nval <= 0) return;
+    if (p.splits > 1) {
+        float *w = p.ws + ((int64_t)blockIdx.z * p.M + i) * p.N + j;
+        if (nval == 4 && (p.N & 3) == 0) {
+            *reinterpret_cast<f32x4 *>(w) = v;
+        } else {
+            for (int e = 0; e < nval; ++e) w[e] = v[e];
+        }
+        return;
+    }
+    const bool whole = nval == 4 && p.cd_vec;
+    if (p.C) {
+        const int64_t off = (int64_t)i * p.ldc + j;
+        if (p.out_dtype == DT_F32) {
+            const float *c = reinterpret_cast<const float *>(p.C) + off;
+            if (whole) {
+                v += *reinterpret_cast<const f32x4 *>(c);
+            } else {
+                for (int e = 0; e < nval; ++e) v[e] += c[e];
+            }
+        } else {
+            const uint16_t *c = reinterpret_cast<const uint16_t *>(p.C) + off;
+            uint16_t h[4] = {0, 0, 0, 0};
+            if (whole) {
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(c);
+                h[0] = (uint16_t)lo16(w[0]); h[1] = (uint16_t)hi16(w[0]);
+                h[2] = (uint16_t)lo16(w[1]); h[3] = (uint16_t)hi16(w[1]);
+            } else {
+                for (int e = 0; e < nval; ++e) h[e] = c[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] += (p.out_dtype == DT_F16) ? (float)__builtin_bit_cast(_Float16, h[e])
+                                                : __uint_as_float((uint32_t)h[e] << 16);
+        }
+    }
+    const int64_t off = (int64_t)i * p.ldd + j;
+    if (p.out_dtype == DT_F32) {
+        if (p.satf) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (__builtin_isnan(v[e])) v[e] = 0.0f;
+                else if (__builtin_isinf(v[e])) v[e] = v[e] > 0 ? 3.402823466e38f : -3.402823466e38f;
+            }
+        }
+        float *d = reinterpret_cast<float *>(p.D) + off;
+        if (whole) {
+            *reinterpret_cast<f32x4 *>(d) = v;
+        } else {
+            for (int e = 0; e < nval; ++e) d[e] = v[e];
+        }
+    } else {
+        const bool f16 = p.out_dtype == DT_F16;
+        const uint16_t expo = f16 ? 0x7c00u : 0x7f80u;
+        const uint16_t mx = f16 ? 0x7bffu : 0x7f7fu;
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = f16 ? __builtin_bit_cast(uint16_t, (_Float16)v[e]) : f32_to_bf16_rne(v[e]);
+            if (p.satf && (h[e] & expo) == expo)
+                h[e] = (h[e] & (uint16_t)(~expo & 0x7fffu)) ? (uint16_t)0
+                                                            : (uint16_t)((h[e] & 0x8000u) | mx);
+        }
+        uint16_t *d = reinterpret_cast<uint16_t *>(p.D) + off;
+        if (whole) {
+            *reinterpret_cast<u32x2 *>(d) =
+                u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        } else {
+            for (int e = 0; e < nval; ++e) d[e] = h[e];
+        }
+    }
+}
+
 // ------------------------------------------------------------ tile mapping
 // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
 // w % 8).  Renumber them so each XCD receives a contiguous range of tiles,
@@ -380,15 +570,182 @@ __device__ __forceinline__ void map_tile(const Params &p, int w, int &tm, int &t
     tn = t_in / gsize;
 }
 
-// ------------------------------------------------------------------ kernel
-template <class CF, bool BF, bool A_KC, bool B_KC>
-__global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
+// ------------------------------------------------------------------ K loop
+// Software-pipelined K loop over two LDS stages (cur = t & 1), KS MFMA steps
+// per K-tile, operand fragments double-buffered by step parity.  Iteration t:
+//   step 0      : store K-tile t+1 (in registers) to LDS[cur^1]
+//   step 1      : issue the global loads of K-tile t+2
+//   step s < KS-1: read the fragments of step s+1 from LDS[cur]
+//   step KS-1   : barrier, then read step 0 of K-tile t+1 from LDS[cur^1]
+//   every step  : the MFMAs of step s
+// One barrier per K-tile orders this tile's LDS reads before the overwrite
+// two tiles later and the stores of tile t+1 before its reads.  The body has
+// no branches: past the last K-tile the loads re-read it and the stores and
+// reads go to the idle stage.
+template <class CF, bool BF, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
+__device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg, int kend,
+                                       typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
+                                       u32x4 *sA, u32x4 *sB, int tid) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, CH = CF::CH;
     constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN, THREADS = CF::THREADS;
+    constexpr int KS = BK / CF::KSTEP;           // MFMA steps per K-tile
+    constexpr int KCH = CF::KSTEP / 8;            // LDS chunks per MFMA step
+    static_assert(KS % 2 == 0 && KS >= 4, "fragment slots alternate across K-tiles; the"
+                  " store, load and barrier steps are distinct");
     using LA = typename std::conditional<A_KC, LoaderKC<BM, BK, THREADS>,
                                          LoaderRC<BM, BK, THREADS>>::type;
     using LB = typename std::conditional<B_KC, LoaderKC<BN, BK, THREADS>,
                                          LoaderRC<BN, BK, THREADS>>::type;
+
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    if (nk <= 0) return;
+
+    LA la;
+    LB lb;
+    la.init(tid, p.lda, m0, p.M);
+    lb.init(tid, p.ldb, n0, p.N);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+    auto gload = [&](int kt) {
+        const int k0 = kbeg + kt * BK;
+        if constexpr (VEC) {
+            la.load(ra, k0, p.lda);
+            lb.load(rb, k0, p.ldb);
+            if constexpr (RAGGED) {  // only the prologue's stores use this directly
+                la.mask(k0, kend);
+                lb.mask(k0, kend);
+            }
+        } else {
+            la.load_checked(p.A, p.lda, m0, k0, p.M, kend, tid);
+            lb.load_checked(p.B, p.ldb, n0, k0, p.N, kend, tid);
+        }
+    };
+
+    // Per-lane LDS byte offsets of each fragment at step 0; step s XORs in
+    // s*KCH chunks (the chunk bits of s and of the lane never overlap).
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+    uint32_t a_off[TM], b_off[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm * CF::WTM + i * MF + (lane & (MF - 1));
+        a_off[i] = (uint32_t)(r * CH + ((lane / MF) ^ swz(r))) * 16u;
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int r = wn * CF::WTN + j * MF + (lane & (MF - 1));
+        b_off[j] = (uint32_t)(r * CH + ((lane / MF) ^ swz(r))) * 16u;
+    }
+
+    u32x4 fa[2][TM], fb[2][TN];
+    // fragment f (A fragments first, then B) of step ks into slot sl
+    auto read_one = [&](int buf, auto ks_tag, auto sl_tag, auto f_tag) {
+        constexpr int ks = decltype(ks_tag)::value, sl = decltype(sl_tag)::value;
+        constexpr int f = decltype(f_tag)::value;
+        constexpr uint32_t kx = (uint32_t)(ks * KCH * 16);
+        if constexpr (f < TM) {
+            const char *ab = reinterpret_cast<const char *>(sA + buf * BM * CH);
+            fa[sl][f] = *reinterpret_cast<const u32x4 *>(ab + (a_off[f] ^ kx));
+        } else {
+            const char *bb = reinterpret_cast<const char *>(sB + buf * BN * CH);
+            fb[sl][f - TM] = *reinterpret_cast<const u32x4 *>(bb + (b_off[f - TM] ^ kx));
+        }
+    };
+    auto mfma_one = [&](auto sl_tag, auto m_tag) {
+        constexpr int sl = decltype(sl_tag)::value, m = decltype(m_tag)::value;
+        constexpr int i = m / TN, j = m % TN;
+        if constexpr (MF == 32)
+            acc[i][j] = mfma32<BF>(fa[sl][i], fb[sl][j], acc[i][j]);
+        else
+            acc[i][j] = mfma16<BF>(fa[sl][i], fb[sl][j], acc[i][j]);
+    };
+    auto store_one = [&](int buf, auto w_tag) {
+        constexpr int w = decltype(w_tag)::value;
+        if constexpr (w < LA::NSTORE)
+            la.template store_one<w>(sA + buf * BM * CH, tid);
+        else
+            lb.template store_one<w - LA::NSTORE>(sB + buf * BN * CH, tid);
+    };
+    auto load_one = [&](int k0, auto g_tag) {
+        constexpr int g = decltype(g_tag)::value;
+        if constexpr (g < LA::NLOAD)
+            la.template load_one<g>(ra, k0, p.lda);
+        else
+            lb.template load_one<g - LA::NLOAD>(rb, k0, p.ldb);
+    };
+
+    // prologue: K-tile 0 in LDS[0], K-tile 1 in registers, step 0 fragments
+    gload(0);
+    la.store(sA, tid);
+    lb.store(sB, tid);
+    gload(nk > 1 ? 1 : 0);
+    __syncthreads();
+    Unroll<0, TM + TN>::run([&](auto f) {
+        read_one(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, f);
+    });
+
+    constexpr int NM = TM * TN, NR = TM + TN;
+    constexpr int NW = LA::NSTORE + LB::NSTORE, NV = LA::NLOAD + LB::NLOAD;
+    for (int t = 0; t < nk; ++t) {
+        const int cur = t & 1;
+        const int k_next = kbeg + min(t + 2, nk - 1) * BK;  // K-tile loaded in step 1
+        if constexpr (!VEC) {
+            // element-wise path: stores and loads as plain blocks
+            la.store(sA + (cur ^ 1) * BM * CH, tid);
+            lb.store(sB + (cur ^ 1) * BN * CH, tid);
+            gload(min(t + 2, nk - 1));
+        } else if constexpr (RAGGED) {
+            const int k_st = kbeg + min(t + 1, nk - 1) * BK;  // K-tile stored in step 0
+            la.mask(k_st, kend);
+            lb.mask(k_st, kend);
+        }
+        Unroll<0, KS>::run([&](auto ks_tag) {
+            constexpr int ks = decltype(ks_tag)::value;
+            constexpr int sl = ks & 1;
+            if constexpr (ks == KS - 1) {
+                // every LDS read of this K-tile and store of the next is done
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // One MFMA, then its share of the step's other instructions, in
+            // source order (the fences keep the compiler from regrouping):
+            //   step 0: the stores of K-tile t+1, step 1: the loads of K-tile
+            //   t+2, every step: the fragment reads of the next step.
+            Unroll<0, NM>::run([&](auto m_tag) {
+                constexpr int m = decltype(m_tag)::value;
+                mfma_one(std::integral_constant<int, sl>{}, m_tag);
+                if constexpr (VEC && ks == 0) {
+                    Unroll<m * NW / NM, (m + 1) * NW / NM>::run(
+                        [&](auto w) { store_one(cur ^ 1, w); });
+                }
+                if constexpr (VEC && ks == 1) {
+                    Unroll<m * NV / NM, (m + 1) * NV / NM>::run(
+                        [&](auto g) { load_one(k_next, g); });
+                }
+                Unroll<m * NR / NM, (m + 1) * NR / NM>::run([&](auto f) {
+                    if constexpr (ks + 1 < KS)
+                        read_one(cur, std::integral_constant<int, ks + 1>{},
+                                 std::integral_constant<int, sl ^ 1>{}, f);
+                    else
+                        read_one(cur ^ 1, std::integral_constant<int, 0>{},
+                                 std::integral_constant<int, 0>{}, f);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    }
+}
+
+// ------------------------------------------------------------------ kernel
+// VEC selects the vector (aligned) or the element-wise (unaligned) loads and
+// RAGGED whether the vector loads mask k >= kend; each combination is its own
+// kernel, with a single K loop to allocate registers for.
+template <class CF, bool BF, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
+__global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
+    constexpr int BM = CF::BM, BN = CF::BN, CH = CF::CH;
+    constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
     using Acc = typename AccT<MF>::type;
 
     __shared__ u32x4 smem[2 * (BM + BN) * CH];
@@ -405,11 +762,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
 
     const int kbeg = blockIdx.z * p.k_per_split;
     const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-    const bool interior = p.vec_ok && (m0 + BM <= p.M) && (n0 + BN <= p.N);
 
-    LA la;
-    LB lb;
     Acc acc[TM][TN];
     Unroll<0, TM>::run([&](auto ii) {
         Unroll<0, TN>::run([&](auto jj) {
@@ -417,99 +770,38 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         });
     });
 
-    auto load_tiles = [&](int kt) {
-        const int k0 = kbeg + kt * BK;
-        if (interior && k0 + BK <= kend) {
-            la.load_fast(p.A, p.lda, m0, k0, tid);
-            lb.load_fast(p.B, p.ldb, n0, k0, tid);
-        } else {
-            la.load_checked(p.A, p.lda, m0, k0, p.M, kend, p.vec_ok, tid);
-            lb.load_checked(p.B, p.ldb, n0, k0, p.N, kend, p.vec_ok, tid);
-        }
-    };
+    k_loop<CF, BF, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
 
-    if (nk > 0) {
-        load_tiles(0);
-        la.store(sA, tid);
-        lb.store(sB, tid);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_tiles(kt + 1);  // in flight during the MFMAs below
-
-        const u32x4 *a_s = sA + cur * BM * CH;
-        const u32x4 *b_s = sB + cur * BN * CH;
-#pragma unroll
-        for (int ks = 0; ks < BK / CF::KSTEP; ++ks) {
-            u32x4 af[TM], bf[TN];
-            const int chunk = ks * (CF::KSTEP / 8) + lane / MF;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * CF::WTM + i * MF + (lane & (MF - 1));
-                af[i] = a_s[r * CH + (chunk ^ swz(r))];
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = wn * CF::WTN + j * MF + (lane & (MF - 1));
-                bf[j] = b_s[r * CH + (chunk ^ swz(r))];
-            }
-            Unroll<0, TM>::run([&](auto ii) {
-                Unroll<0, TN>::run([&](auto jj) {
-                    constexpr int i = decltype(ii)::value, j = decltype(jj)::value;
-                    if constexpr (MF == 32)
-                        acc[i][j] = mfma32<BF>(af[i], bf[j], acc[i][j]);
-                    else
-                        acc[i][j] = mfma16<BF>(af[i], bf[j], acc[i][j]);
-                });
-            });
-        }
-
-        if (kt + 1 < nk) {
-            la.store(sA + (cur ^ 1) * BM * CH, tid);
-            lb.store(sB + (cur ^ 1) * BN * CH, tid);
-        }
-        __syncthreads();
-    }
-
-    // Epilogue: split-K slices store raw fp32 partial sums (OUT = -1);
-    // otherwise C add, convert, satf and store.  Interior tiles skip the
-    // bounds checks.
-    const bool full_tile = (m0 + BM <= p.M) && (n0 + BN <= p.N);
-    auto epilogue = [&](auto out_tag, auto check_tag) {
-        constexpr int OUT = decltype(out_tag)::value;
-        constexpr bool CHECK = decltype(check_tag)::value;
+    // Epilogue through LDS (free once the K loop's last barrier has passed):
+    // each wave stages one MF-row block of its accumulators at a time in its
+    // own region (fp32, row-major, rows padded against bank conflicts), then
+    // reads it back four columns per lane, so the C reads and D writes are
+    // row-contiguous vector accesses.
+    {
+        constexpr int WTN = CF::WTN, NREG = AccT<MF>::N;
+        constexpr int SROW = WTN + 8;          // floats per staged row
+        constexpr int LPR = WTN / 4;           // lanes per staged row
+        constexpr int RPP = 64 / LPR;          // rows per pass of the wave
+        static_assert(64 % LPR == 0, "lanes per staged row");
+        static_assert(CF::WAVES_M * CF::WAVES_N * MF * SROW * 4 <= (int)sizeof(smem),
+                      "staging fits in the operand buffers");
+        float *stage = reinterpret_cast<float *>(smem) + wave * MF * SROW;
+        const int row0 = m0 + wm * CF::WTM, col0 = n0 + wn * WTN;
+        const int c4 = (lane % LPR) * 4;
         Unroll<0, TM>::run([&](auto ii) {
+            constexpr int i = decltype(ii)::value;
             Unroll<0, TN>::run([&](auto jj) {
-                Unroll<0, AccT<MF>::N>::run([&](auto rr) {
-                    constexpr int i = decltype(ii)::value, j = decltype(jj)::value;
-                    constexpr int r = decltype(rr)::value;
-                    const int gi = m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane, r);
-                    const int gj = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane);
-                    if (!CHECK || (gi < p.M && gj < p.N)) {
-                        if constexpr (OUT < 0)
-                            p.ws[((int64_t)blockIdx.z * p.M + gi) * p.N + gj] = acc[i][j][r];
-                        else
-                            finish_store_t<OUT>(p, gi, gj, acc[i][j][r]);
-                    }
+                Unroll<0, NREG>::run([&](auto rr) {
+                    constexpr int j = decltype(jj)::value, r = decltype(rr)::value;
+                    stage[acc_row<MF>(lane, r) * SROW + j * MF + acc_col<MF>(lane)] =
+                        acc[i][j][r];
                 });
             });
+            for (int rr = lane / LPR; rr < MF; rr += RPP) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + rr * SROW + c4);
+                finish4(p, row0 + i * MF + rr, col0 + c4, v);
+            }
         });
-    };
-    using IC_T = std::integral_constant<bool, true>;
-    using IC_F = std::integral_constant<bool, false>;
-    if (p.splits > 1) {
-        epilogue(std::integral_constant<int, -1>{}, IC_T{});
-    } else if (p.out_dtype == DT_F32) {
-        if (full_tile) epilogue(std::integral_constant<int, DT_F32>{}, IC_F{});
-        else epilogue(std::integral_constant<int, DT_F32>{}, IC_T{});
-    } else if (p.out_dtype == DT_F16) {
-        if (full_tile) epilogue(std::integral_constant<int, DT_F16>{}, IC_F{});
-        else epilogue(std::integral_constant<int, DT_F16>{}, IC_T{});
-    } else {
-        if (full_tile) epilogue(std::integral_constant<int, DT_BF16>{}, IC_F{});
-        else epilogue(std::integral_constant<int, DT_BF16>{}, IC_T{});
     }
 }
 
