@@ -18,7 +18,6 @@ region starts.  Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,18 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s (2MNK/t) and % of MI355X fp16 MFMA peak, 4096³ fp16→fp32"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_f16.json")
-
-
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; counter-derived traffic is reported only when it
-    was measured on exactly these sources."""
-    csrc = os.path.join(ROOT, "dense_mixed_precision_tiled_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()[:16]
+COPY_BYTES = 256 << 20  # size of the calibration copy
 
 
 def load_traffic():
@@ -50,6 +38,7 @@ def load_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from dense_mixed_precision_tiled_amd.rocprof_summary import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
@@ -88,6 +77,42 @@ def cpu_baseline(prob, target_s: float):
     }
 
 
+# name -> (generator, description, roofline bound)
+WORKLOADS = {
+    "4096_f16": ("w_4096_f16", "M=N=K=4096 GEMM, fp16 row-major A and B (uniform[-1,1], "
+                 "seeded), fp32 accumulate, fp32 D, C=0", "mfma"),
+    "256_f16": ("w_256", "M=N=K=256 GEMM, fp16 row-major A and B (uniform[-1,1]), fp32 D, C=0",
+                "mfma"),
+    "4096_bf16_inplace": ("w_4096_bf16_inplace", "M=N=K=4096 GEMM, bf16 row-major A, bf16 "
+                          "col-major B (normal), fp32 C updated in place", "mfma"),
+    "hgemm_satf0": ("w_hgemm", "HGEMM 3999x4001x4104, fp16 accumulate/out, padded ld, 1% of "
+                    "A rows x2048, satf=0", "mfma"),
+    "hgemm_satf1": ("w_hgemm", "HGEMM 3999x4001x4104, fp16 accumulate/out, padded ld, 1% of "
+                    "A rows x2048, satf=1", "mfma"),
+    "wide": ("w_wide", "M=N=16384, K=1024 GEMM, fp16 row-major in, fp32 D", "mfma"),
+    "skinny": ("w_skinny", "M=16, N=K=16384 GEMM, fp16 row-major in, fp32 D", "hbm"),
+}
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def make_workload(W, name):
+    gen, desc, bound = WORKLOADS[name]
+    if name.startswith("hgemm"):
+        prob = getattr(W, gen)(int(name[-1]), "uniform")
+    elif name == "4096_bf16_inplace":
+        prob = getattr(W, gen)("normal")
+    else:
+        prob = getattr(W, gen)("uniform")
+    return prob, desc, bound
+
+
+def algorithmic_bytes(prob) -> int:
+    """Compulsory HBM bytes: A and B once, C read once (if any), D written once."""
+    osz = 4 if prob.out_dtype == 0 else 2
+    c = prob.M * prob.N * osz if prob.C is not None else 0
+    return 2 * prob.M * prob.K + 2 * prob.K * prob.N + c + prob.M * prob.N * osz
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +120,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--workload", default="4096_f16", choices=sorted(WORKLOADS),
+                    help="workload to time (default: the headline 4096^3 fp16->fp32)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -114,17 +143,32 @@ def main():
         sys.exit(1)
     lg.library()
 
-    prob = W.w_4096_f16("uniform")
+    prob, desc, bound = make_workload(W, args.workload)
     dev = torch.device("cuda:0")
     A = torch.from_numpy(prob.A.view(np.int16)).to(dev)
     B = torch.from_numpy(prob.B.view(np.int16)).to(dev)
-    D = torch.empty(prob.D.shape, dtype=torch.float32, device=dev)
+    D = torch.from_numpy(prob.D.view(np.int16) if prob.D.dtype == np.uint16 else prob.D).to(dev)
+    if prob.inplace:
+        C = D
+    elif prob.C is not None:
+        C = torch.from_numpy(prob.C.view(np.int16) if prob.C.dtype == np.uint16 else prob.C).to(dev)
+    else:
+        C = None
     stream = torch.cuda.current_stream()
     call = (prob.M, prob.N, prob.K, A.data_ptr(), prob.lda, prob.layoutA, B.data_ptr(),
-            prob.ldb, prob.layoutB, None, prob.ldc, D.data_ptr(), prob.ldd, prob.in_dtype,
-            prob.acc_dtype, prob.out_dtype, prob.satf, stream.cuda_stream)
+            prob.ldb, prob.layoutB, None if C is None else C.data_ptr(), prob.ldc, D.data_ptr(),
+            prob.ldd, prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf,
+            stream.cuda_stream)
     cfg = lg.gemm_select_config(prob.M, prob.N, prob.K, prob.layoutA, prob.layoutB,
                                 prob.in_dtype, prob.acc_dtype, prob.out_dtype)
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         st = lg.gemm_run(*call)
@@ -151,10 +195,19 @@ def main():
     flop = float(prob.flops)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (mean_ms * 1e-3) / 1e12
-    traffic = load_traffic()
+    traffic = load_traffic() if args.workload == "4096_f16" else None
+    nbytes = algorithmic_bytes(prob)
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4)}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "4096_f16" else
+        "GEMM TFLOP/s (2MNK/t), workload %s" % args.workload,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
@@ -165,29 +218,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16" if prob.in_dtype == 2 else "f16",
         "data": "synthetic",
         "config": {
-            "workload": "M=N=K=4096 GEMM, fp16 row-major A and B (uniform[-1,1], seeded), "
-                        "fp32 accumulate, fp32 D, C=0",
+            "workload": desc,
             "M": prob.M, "N": prob.N, "K": prob.K,
             "tile_config": lg.gemm_config_name(cfg),
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_TFLOPS, 4),
+        "roofline": dict(roof, **{
             "traffic": traffic,
+            "algorithmic_bytes": nbytes,
             "kernel": "gemm_mfma_kernel<%s>" % lg.gemm_config_name(cfg),
             "launch_ms_mean": round(mean_ms, 5),
             "launch_ms_min": round(min(durations_ms), 5),
             "launch_ms_median": round(sorted(durations_ms)[len(durations_ms) // 2], 5),
-        },
+        }),
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "4096_f16":
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -20,10 +20,20 @@ using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16, 1>;
 typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
                                 dim3 grid, hipStream_t stream);
 
-hipError_t launch_large(const Params &, int, int, int, dim3, hipStream_t);
-hipError_t launch_medium(const Params &, int, int, int, dim3, hipStream_t);
-hipError_t launch_small(const Params &, int, int, int, dim3, hipStream_t);
-hipError_t launch_skinny(const Params &, int, int, int, dim3, hipStream_t);
+// one translation unit per (entry, input dtype): kernels_<entry>_<dtype>.hip
+#define LIBGEMM_DECLARE_LAUNCH(name)                                                   \
+    hipError_t launch_##name##_f16(const Params &, int, int, dim3, hipStream_t);     \
+    hipError_t launch_##name##_bf16(const Params &, int, int, dim3, hipStream_t);    \
+    inline hipError_t launch_##name(const Params &p, int bf, int akc, int bkc, dim3 grid, \
+                                    hipStream_t s) {                                  \
+        return bf ? launch_##name##_bf16(p, akc, bkc, grid, s)                        \
+                  : launch_##name##_f16(p, akc, bkc, grid, s);                        \
+    }
+LIBGEMM_DECLARE_LAUNCH(large)
+LIBGEMM_DECLARE_LAUNCH(medium)
+LIBGEMM_DECLARE_LAUNCH(small)
+LIBGEMM_DECLARE_LAUNCH(skinny)
+#undef LIBGEMM_DECLARE_LAUNCH
 
 template <class CF, bool BF, bool AKC, bool BKC>
 hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
@@ -48,12 +58,6 @@ hipError_t launch_layouts(const Params &p, int akc, int bkc, dim3 grid, hipStrea
                    : launch_one<CF, BF, true, false>(p, grid, s);
     return bkc ? launch_one<CF, BF, false, true>(p, grid, s)
                : launch_one<CF, BF, false, false>(p, grid, s);
-}
-
-template <class CF>
-hipError_t launch_cfg(const Params &p, int bf, int akc, int bkc, dim3 grid, hipStream_t s) {
-    return bf ? launch_layouts<CF, true>(p, akc, bkc, grid, s)
-              : launch_layouts<CF, false>(p, akc, bkc, grid, s);
 }
 
 }  // namespace libgemm

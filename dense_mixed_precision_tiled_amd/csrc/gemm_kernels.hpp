@@ -407,18 +407,21 @@ template <int MF> struct AccT;
 template <> struct AccT<32> { typedef f32x16 type; static constexpr int N = 16; };
 template <> struct AccT<16> { typedef f32x4 type; static constexpr int N = 4; };
 
-// Position of accumulator register r of `lane` inside an MF x MF tile.
-// 32x32: column lane%32, row 8*(r/4) + 4*(lane/32) + r%4.
-// 16x16: column lane%16, row 4*(lane/16) + r.
+// Position of accumulator register r of `lane` inside an MF x MF tile of D.
+// The MFMA output layout (column lane % MF; rows 8*(r/4) + 4*(lane/32) + r%4
+// for 32x32, 4*(lane/16) + r for 16x16) describes the transposed tile here,
+// because the operands are passed B first.  So lane holds D row lane % MF,
+// and registers 4g..4g+3 hold four consecutive D columns starting at
+// acc_col(lane, g).
 template <int MF>
-__device__ __forceinline__ int acc_row(int lane, int r) {
+__device__ __forceinline__ int acc_row(int lane) { return lane & (MF - 1); }
+template <int MF>
+__device__ __forceinline__ int acc_col(int lane, int g) {
     if constexpr (MF == 32)
-        return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        return 8 * g + 4 * (lane >> 5);
     else
-        return 4 * (lane >> 4) + r;
+        return 4 * (lane >> 4);
 }
-template <int MF>
-__device__ __forceinline__ int acc_col(int lane) { return lane & (MF - 1); }
 
 // ---------------------------------------------------------------- epilogue
 __device__ __forceinline__ float load_c(const Params &p, int64_t i, int64_t j) {
@@ -471,81 +474,93 @@ __device__ __forceinline__ void finish_store(const Params &p, int64_t i, int64_t
     else finish_store_t<DT_BF16>(p, i, j, v);
 }
 
-// Four consecutive outputs D(i, j..j+3) from fp32 sums v: split-K slices
-// store the raw sums; otherwise C is added, the result rounded once to the
-// output dtype, satf applied, and the group stored with one vector store
-// when it is whole and aligned.  Outputs outside M x N are skipped.
+// satf on a rounded fp32 value: +-Inf -> +-MAX_NORM, NaN -> +0.
+__device__ __forceinline__ float satf_f32(float x) {
+    if (__builtin_isnan(x)) return 0.0f;
+    if (__builtin_isinf(x)) return x > 0 ? 3.402823466e38f : -3.402823466e38f;
+    return x;
+}
+
+// fp32 -> 16-bit output pattern (RNE), then satf when asked.
+template <int OUT>
+__device__ __forceinline__ uint32_t to_out16(float x, bool satf) {
+    constexpr uint32_t expo = (OUT == DT_F16) ? 0x7c00u : 0x7f80u;
+    constexpr uint32_t mx = (OUT == DT_F16) ? 0x7bffu : 0x7f7fu;
+    uint32_t h = (OUT == DT_F16) ? (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x)
+                                 : (uint32_t)f32_to_bf16_rne(x);
+    if (satf && (h & expo) == expo)
+        h = (h & (~expo & 0x7fffu)) ? 0u : ((h & 0x8000u) | mx);
+    return h;
+}
+
+template <int OUT>
+__device__ __forceinline__ float from_out16(uint32_t h) {
+    return (OUT == DT_F16) ? (float)__builtin_bit_cast(_Float16, (uint16_t)h)
+                           : __uint_as_float(h << 16);
+}
+
+// Four consecutive outputs D(i, j..j+3) from fp32 sums v.  OUT < 0: split-K
+// slice, store the raw sums to the workspace.  Otherwise C is added, the
+// result rounded once to OUT, satf applied and the group stored.  FULL: the
+// group lies inside M x N and C/D allow 4-element vector access, so no
+// checks; else each element is checked and stored alone.
+template <int OUT, bool FULL>
 __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) {
-    const int nval = min(p.N - j, 4);
-    if (i >= p.M || nval <= 0) return;
-    if (p.splits > 1) {
+    const int nval = FULL ? 4 : min(p.N - j, 4);
+    if (!FULL && (i >= p.M || nval <= 0)) return;
+    if constexpr (OUT < 0) {
         float *w = p.ws + ((int64_t)blockIdx.z * p.M + i) * p.N + j;
-        if (nval == 4 && (p.N & 3) == 0) {
+        if (FULL) {
             *reinterpret_cast<f32x4 *>(w) = v;
         } else {
             for (int e = 0; e < nval; ++e) w[e] = v[e];
         }
         return;
-    }
-    const bool whole = nval == 4 && p.cd_vec;
-    if (p.C) {
-        const int64_t off = (int64_t)i * p.ldc + j;
-        if (p.out_dtype == DT_F32) {
-            const float *c = reinterpret_cast<const float *>(p.C) + off;
-            if (whole) {
-                v += *reinterpret_cast<const f32x4 *>(c);
-            } else {
-                for (int e = 0; e < nval; ++e) v[e] += c[e];
-            }
-        } else {
-            const uint16_t *c = reinterpret_cast<const uint16_t *>(p.C) + off;
-            uint16_t h[4] = {0, 0, 0, 0};
-            if (whole) {
-                const u32x2 w = *reinterpret_cast<const u32x2 *>(c);
-                h[0] = (uint16_t)lo16(w[0]); h[1] = (uint16_t)hi16(w[0]);
-                h[2] = (uint16_t)lo16(w[1]); h[3] = (uint16_t)hi16(w[1]);
-            } else {
-                for (int e = 0; e < nval; ++e) h[e] = c[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] += (p.out_dtype == DT_F16) ? (float)__builtin_bit_cast(_Float16, h[e])
-                                                : __uint_as_float((uint32_t)h[e] << 16);
-        }
-    }
-    const int64_t off = (int64_t)i * p.ldd + j;
-    if (p.out_dtype == DT_F32) {
-        if (p.satf) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (__builtin_isnan(v[e])) v[e] = 0.0f;
-                else if (__builtin_isinf(v[e])) v[e] = v[e] > 0 ? 3.402823466e38f : -3.402823466e38f;
-            }
-        }
-        float *d = reinterpret_cast<float *>(p.D) + off;
-        if (whole) {
-            *reinterpret_cast<f32x4 *>(d) = v;
-        } else {
-            for (int e = 0; e < nval; ++e) d[e] = v[e];
-        }
     } else {
-        const bool f16 = p.out_dtype == DT_F16;
-        const uint16_t expo = f16 ? 0x7c00u : 0x7f80u;
-        const uint16_t mx = f16 ? 0x7bffu : 0x7f7fu;
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h[e] = f16 ? __builtin_bit_cast(uint16_t, (_Float16)v[e]) : f32_to_bf16_rne(v[e]);
-            if (p.satf && (h[e] & expo) == expo)
-                h[e] = (h[e] & (uint16_t)(~expo & 0x7fffu)) ? (uint16_t)0
-                                                            : (uint16_t)((h[e] & 0x8000u) | mx);
+        if (p.C) {
+            const int64_t off = (int64_t)i * p.ldc + j;
+            if constexpr (OUT == DT_F32) {
+                const float *c = reinterpret_cast<const float *>(p.C) + off;
+                if (FULL) {
+                    v += *reinterpret_cast<const f32x4 *>(c);
+                } else {
+                    for (int e = 0; e < nval; ++e) v[e] += c[e];
+                }
+            } else {
+                const uint16_t *c = reinterpret_cast<const uint16_t *>(p.C) + off;
+                if (FULL) {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(c);
+                    v[0] += from_out16<OUT>(lo16(w[0]));
+                    v[1] += from_out16<OUT>(hi16(w[0]));
+                    v[2] += from_out16<OUT>(lo16(w[1]));
+                    v[3] += from_out16<OUT>(hi16(w[1]));
+                } else {
+                    for (int e = 0; e < nval; ++e) v[e] += from_out16<OUT>(c[e]);
+                }
+            }
         }
-        uint16_t *d = reinterpret_cast<uint16_t *>(p.D) + off;
-        if (whole) {
-            *reinterpret_cast<u32x2 *>(d) =
-                u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        const int64_t off = (int64_t)i * p.ldd + j;
+        if constexpr (OUT == DT_F32) {
+            if (p.satf) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = satf_f32(v[e]);
+            }
+            float *d = reinterpret_cast<float *>(p.D) + off;
+            if (FULL) {
+                *reinterpret_cast<f32x4 *>(d) = v;
+            } else {
+                for (int e = 0; e < nval; ++e) d[e] = v[e];
+            }
         } else {
-            for (int e = 0; e < nval; ++e) d[e] = h[e];
+            const bool sf = p.satf != 0;
+            uint16_t *d = reinterpret_cast<uint16_t *>(p.D) + off;
+            if (FULL) {
+                *reinterpret_cast<u32x2 *>(d) =
+                    u32x2{to_out16<OUT>(v[0], sf) | (to_out16<OUT>(v[1], sf) << 16),
+                          to_out16<OUT>(v[2], sf) | (to_out16<OUT>(v[3], sf) << 16)};
+            } else {
+                for (int e = 0; e < nval; ++e) d[e] = (uint16_t)to_out16<OUT>(v[e], sf);
+            }
         }
     }
 }
@@ -656,10 +671,13 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     auto mfma_one = [&](auto sl_tag, auto m_tag) {
         constexpr int sl = decltype(sl_tag)::value, m = decltype(m_tag)::value;
         constexpr int i = m / TN, j = m % TN;
+        // B fragment as the MFMA's first operand: the instruction then forms
+        // the transposed tile, whose rows (D columns) land in consecutive
+        // accumulator registers of one lane (see acc_col)
         if constexpr (MF == 32)
-            acc[i][j] = mfma32<BF>(fa[sl][i], fb[sl][j], acc[i][j]);
+            acc[i][j] = mfma32<BF>(fb[sl][j], fa[sl][i], acc[i][j]);
         else
-            acc[i][j] = mfma16<BF>(fa[sl][i], fb[sl][j], acc[i][j]);
+            acc[i][j] = mfma16<BF>(fb[sl][j], fa[sl][i], acc[i][j]);
     };
     auto store_one = [&](int buf, auto w_tag) {
         constexpr int w = decltype(w_tag)::value;
@@ -687,17 +705,24 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     });
 
     constexpr int NM = TM * TN, NR = TM + TN;
-    constexpr int NW = LA::NSTORE + LB::NSTORE, NV = LA::NLOAD + LB::NLOAD;
+    constexpr int NW = LA::NSTORE + LB::NSTORE;
+    // Store schedule: the NW stores of K-tile t+1 are spread evenly over the
+    // MFMA slots of steps 0..KS-2 (slot s = step*NM + m), A stores first.  A
+    // K-contiguous operand's load of K-tile t+2 follows the store that frees
+    // its registers; an R-contiguous operand's block is reloaded right after
+    // the last of its 8 (transposing) stores.
+    constexpr int NSLOT = (KS - 1) * NM;
+    auto store_slot = [](int w) { return w * NSLOT / NW; };
     for (int t = 0; t < nk; ++t) {
         const int cur = t & 1;
-        const int k_next = kbeg + min(t + 2, nk - 1) * BK;  // K-tile loaded in step 1
+        const int k_next = kbeg + min(t + 2, nk - 1) * BK;  // K-tile being loaded
         if constexpr (!VEC) {
             // element-wise path: stores and loads as plain blocks
             la.store(sA + (cur ^ 1) * BM * CH, tid);
             lb.store(sB + (cur ^ 1) * BN * CH, tid);
             gload(min(t + 2, nk - 1));
         } else if constexpr (RAGGED) {
-            const int k_st = kbeg + min(t + 1, nk - 1) * BK;  // K-tile stored in step 0
+            const int k_st = kbeg + min(t + 1, nk - 1) * BK;  // K-tile stored this iteration
             la.mask(k_st, kend);
             lb.mask(k_st, kend);
         }
@@ -709,20 +734,37 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
                 __syncthreads();
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // One MFMA, then its share of the step's other instructions, in
-            // source order (the fences keep the compiler from regrouping):
-            //   step 0: the stores of K-tile t+1, step 1: the loads of K-tile
-            //   t+2, every step: the fragment reads of the next step.
+            // One MFMA, then the stores and loads scheduled in its slot, then
+            // its share of the next step's fragment reads, in source order
+            // (the fences keep the compiler from regrouping them).
             Unroll<0, NM>::run([&](auto m_tag) {
                 constexpr int m = decltype(m_tag)::value;
+                constexpr int slot = ks * NM + m;
                 mfma_one(std::integral_constant<int, sl>{}, m_tag);
-                if constexpr (VEC && ks == 0) {
-                    Unroll<m * NW / NM, (m + 1) * NW / NM>::run(
-                        [&](auto w) { store_one(cur ^ 1, w); });
-                }
-                if constexpr (VEC && ks == 1) {
-                    Unroll<m * NV / NM, (m + 1) * NV / NM>::run(
-                        [&](auto g) { load_one(k_next, g); });
+                if constexpr (VEC) {
+                    Unroll<0, NW>::run([&](auto w_tag) {
+                        constexpr int w = decltype(w_tag)::value;
+                        if constexpr (w * NSLOT / NW == slot) {
+                            store_one(cur ^ 1, w_tag);
+                            if constexpr (w < LA::NSTORE) {
+                                if constexpr (A_KC) {
+                                    load_one(k_next, w_tag);
+                                } else if constexpr (w % 8 == 7) {
+                                    Unroll<(w / 8) * LA::KB, (w / 8 + 1) * LA::KB>::run(
+                                        [&](auto g) { load_one(k_next, g); });
+                                }
+                            } else {
+                                constexpr int wb = w - LA::NSTORE;
+                                if constexpr (B_KC) {
+                                    load_one(k_next, std::integral_constant<int, LA::NLOAD + wb>{});
+                                } else if constexpr (wb % 8 == 7) {
+                                    Unroll<LA::NLOAD + (wb / 8) * LB::KB,
+                                           LA::NLOAD + (wb / 8 + 1) * LB::KB>::run(
+                                        [&](auto g) { load_one(k_next, g); });
+                                }
+                            }
+                        }
+                    });
                 }
                 Unroll<m * NR / NM, (m + 1) * NR / NM>::run([&](auto f) {
                     if constexpr (ks + 1 < KS)
@@ -736,6 +778,7 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
             });
         });
     }
+    (void)store_slot;
 }
 
 // ------------------------------------------------------------------ kernel
@@ -772,13 +815,41 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
 
     k_loop<CF, BF, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
 
-    // Epilogue through LDS (free once the K loop's last barrier has passed):
-    // each wave stages one MF-row block of its accumulators at a time in its
-    // own region (fp32, row-major, rows padded against bank conflicts), then
-    // reads it back four columns per lane, so the C reads and D writes are
-    // row-contiguous vector accesses.
+    // Epilogue.  Each lane owns 4 consecutive columns of one row per register
+    // group.  Interior tiles with vector-friendly C/D finish and store those
+    // straight from registers (C add, convert, satf, one vector store per
+    // group).  Edge tiles, split-K slices and unaligned C/D stage the tile
+    // through LDS and finish it row by row with element checks.
+    constexpr int NG = AccT<MF>::N / 4;  // 4-column groups per MFMA tile and lane
+    const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.cd_vec && p.splits == 1;
+    auto direct = [&](auto out_tag) {
+        constexpr int OUT = decltype(out_tag)::value;
+        Unroll<0, TM>::run([&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            const int row = m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane);
+            Unroll<0, TN>::run([&](auto jj) {
+                constexpr int j = decltype(jj)::value;
+                Unroll<0, NG>::run([&](auto gg) {
+                    constexpr int g = decltype(gg)::value;
+                    const int col = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
+                    const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    finish4<OUT, true>(p, row, col, v);
+                });
+            });
+        });
+    };
+    if (full) {
+        if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
+        else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
+        else direct(std::integral_constant<int, DT_BF16>{});
+        return;
+    }
+    // staged path: one MF-row block per wave at a time in the wave's own LDS
+    // region (free: the K loop's last barrier has passed), rows padded
+    // against bank conflicts, read back four columns per lane
     {
-        constexpr int WTN = CF::WTN, NREG = AccT<MF>::N;
+        constexpr int WTN = CF::WTN;
         constexpr int SROW = WTN + 8;          // floats per staged row
         constexpr int LPR = WTN / 4;           // lanes per staged row
         constexpr int RPP = 64 / LPR;          // rows per pass of the wave
@@ -791,15 +862,22 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         Unroll<0, TM>::run([&](auto ii) {
             constexpr int i = decltype(ii)::value;
             Unroll<0, TN>::run([&](auto jj) {
-                Unroll<0, NREG>::run([&](auto rr) {
-                    constexpr int j = decltype(jj)::value, r = decltype(rr)::value;
-                    stage[acc_row<MF>(lane, r) * SROW + j * MF + acc_col<MF>(lane)] =
-                        acc[i][j][r];
+                constexpr int j = decltype(jj)::value;
+                Unroll<0, NG>::run([&](auto gg) {
+                    constexpr int g = decltype(gg)::value;
+                    *reinterpret_cast<f32x4 *>(stage + acc_row<MF>(lane) * SROW + j * MF +
+                                               acc_col<MF>(lane, g)) =
+                        f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
                 });
             });
             for (int rr = lane / LPR; rr < MF; rr += RPP) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + rr * SROW + c4);
-                finish4(p, row0 + i * MF + rr, col0 + c4, v);
+                const int gi = row0 + i * MF + rr, gj = col0 + c4;
+                if (p.splits > 1) finish4<-1, false>(p, gi, gj, v);
+                else if (p.out_dtype == DT_F32) finish4<DT_F32, false>(p, gi, gj, v);
+                else if (p.out_dtype == DT_F16) finish4<DT_F16, false>(p, gi, gj, v);
+                else finish4<DT_BF16, false>(p, gi, gj, v);
             }
         });
     }
