@@ -45,9 +45,11 @@ const Entry kTable[] = {
      launch_small},
     {"skinny_16x128x128_w1x4_mfma16x16x32_splitk", CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, 1,
      launch_skinny},
+    {"large8_256x256x64_w2x4_mfma32x32x16", CfgLarge8::BM, CfgLarge8::BN, CfgLarge8::BK, 0,
+     launch_large8},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
-enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3 };
+enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4 };
 
 constexpr int kCUs = 256;  // MI355X compute units
 
@@ -127,7 +129,7 @@ int select_config(int64_t M, int64_t N, int64_t K) {
     (void)K;
     if (M <= CfgSkinny::BM) return CFG_SKINNY;
     const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
-    if (t_large >= 3 * kCUs / 4) return CFG_LARGE;
+    if (t_large >= 3 * kCUs / 4) return CFG_LARGE8;
     const int64_t t_medium = cdiv(M, CfgMedium::BM) * cdiv(N, CfgMedium::BN);
     if (t_medium >= kCUs / 2) return CFG_MEDIUM;
     return CFG_SMALL;

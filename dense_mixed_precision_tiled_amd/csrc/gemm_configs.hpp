@@ -9,6 +9,11 @@ namespace libgemm {
 // Large square-ish problems: 256x256 block tile, 2x2 waves of 128x128
 // (4x4 MFMA 32x32x16 tiles per wave), BK 64, two LDS stages = 128 KiB.
 using CfgLarge = TileCfg<256, 256, 64, 2, 2, 32, 4>;
+// Large problems, eight waves: the same 256x256x64 tile over 2x4 waves of
+// 128x64 (4x2 MFMA tiles per wave), two waves per SIMD.  Each SIMD then
+// alternates between two instruction streams, which hides LDS latency
+// and issue gaps the single-wave schedule exposes.
+using CfgLarge8 = TileCfg<256, 256, 64, 2, 4, 32, 4>;
 // Mid-size problems: 128x128, 2x2 waves of 64x64.
 using CfgMedium = TileCfg<128, 128, 64, 2, 2, 32, 4>;
 // Small problems: 64x64, 2x2 waves of 32x32.
@@ -30,6 +35,7 @@ typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_k
                   : launch_##name##_f16(p, akc, bkc, grid, s);                        \
     }
 LIBGEMM_DECLARE_LAUNCH(large)
+LIBGEMM_DECLARE_LAUNCH(large8)
 LIBGEMM_DECLARE_LAUNCH(medium)
 LIBGEMM_DECLARE_LAUNCH(small)
 LIBGEMM_DECLARE_LAUNCH(skinny)

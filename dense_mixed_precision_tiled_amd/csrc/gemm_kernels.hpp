@@ -723,8 +723,10 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
             gload(min(t + 2, nk - 1));
         } else if constexpr (RAGGED) {
             const int k_st = kbeg + min(t + 1, nk - 1) * BK;  // K-tile stored this iteration
-            la.mask(k_st, kend);
-            lb.mask(k_st, kend);
+            if (k_st + BK > kend) {  // only the last K-tile is ragged (uniform branch)
+                la.mask(k_st, kend);
+                lb.mask(k_st, kend);
+            }
         }
         Unroll<0, KS>::run([&](auto ks_tag) {
             constexpr int ks = decltype(ks_tag)::value;
@@ -766,7 +768,17 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
                         }
                     });
                 }
-                Unroll<m * NR / NM, (m + 1) * NR / NM>::run([&](auto f) {
+                // the next step's fragments in the order that step first uses
+                // them (A row 0, then every B column, then the other A rows:
+                // its first MFMAs need A0 and all of B at once), one per MFMA
+                // from the start of the step, or spread evenly when there are
+                // more fragments than MFMAs
+                constexpr int r_lo = NR <= NM ? (m < NR ? m : NR) : m * NR / NM;
+                constexpr int r_hi = NR <= NM ? (m < NR ? m + 1 : NR) : (m + 1) * NR / NM;
+                Unroll<r_lo, r_hi>::run([&](auto q_tag) {
+                    constexpr int q = decltype(q_tag)::value;
+                    constexpr int fid = (q == 0) ? 0 : (q <= TN ? TM + q - 1 : q - TN);
+                    const auto f = std::integral_constant<int, fid>{};
                     if constexpr (ks + 1 < KS)
                         read_one(cur, std::integral_constant<int, ks + 1>{},
                                  std::integral_constant<int, sl ^ 1>{}, f);

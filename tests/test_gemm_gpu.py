@@ -118,15 +118,29 @@ def test_skinny_16x16384x16384(values, exact):
 
 # ------------------------------------------------- every tile-table entry
 
+# tile-table entries: id -> block tile edge (None: the skinny split-K entry);
+# test_config_ids_match_table checks this against the library's table
+ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256}
+
+
 def _entry_shapes():
     out = []
-    for cid in range(4):
-        if cid == 3:
+    for cid, bm in ENTRY_TILE.items():
+        if bm is None:
             out.append((cid, 13, 3 * 128 - 5, 1100))
         else:
-            bm = (256, 128, 64)[cid]
             out.append((cid, 2 * bm + 17, 3 * bm - 5, 200))
     return out
+
+
+def test_config_ids_match_table():
+    assert lg.gemm_num_configs() == len(ENTRY_TILE)
+    for cid, bm in ENTRY_TILE.items():
+        name = lg.gemm_config_name(cid)
+        if bm is None:
+            assert name.startswith("skinny"), name
+        else:
+            assert name.split("_")[1].startswith("%dx%d" % (bm, bm)), name
 
 
 @pytest.mark.parametrize("cid,M,N,K", _entry_shapes())
@@ -162,10 +176,10 @@ def test_every_entry_output_modes(cid, M, N, K):
                             cid, prob.out_dtype, prob.acc_dtype, prob.inplace, values))
 
 
-@pytest.mark.parametrize("cid", range(4))
+@pytest.mark.parametrize("cid", sorted(ENTRY_TILE))
 def test_unaligned_leading_dims(cid):
     # lda, ldb not multiples of 8 elements: the element-wise load path
-    M, N, K = (37, 45, 77) if cid != 3 else (9, 300, 700)
+    M, N, K = (37, 45, 77) if ENTRY_TILE[cid] is not None else (9, 300, 700)
     for la, lb in ((ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR)):
         a_in = K if la == ROW_MAJOR else M
         b_in = N if lb == ROW_MAJOR else K
