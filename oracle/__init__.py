@@ -16,7 +16,12 @@ arrays through ctypes.  Definitions followed (page title, section):
 * row/col-major addressing with a leading dimension:
   same page sections 3.2 and 4.2;
 * in-place ``C = A*B + C`` and saturate-to-finite:
-  "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释" item (5).
+  "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释" item (5);
+* the extended epilogue ``D = act(alpha*(A x B) + beta*C + bias)`` with row- or
+  column-major C and D (``gemm_ex``): "矩阵乘法优化可视化学习文档" section 6
+  (epilogue fusion) and section 8 (bias/activation at the final store), and the
+  accumulator layouts of "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释"
+  items (3) and (4).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values
 and properties the pages and the mathematics fix (no GPU involved).
@@ -37,6 +42,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 # are part of the call contract, not shared code)
 F32, F16, BF16 = 0, 1, 2
 ROW_MAJOR, COL_MAJOR = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 
 _lib = None
 
@@ -69,6 +75,22 @@ def _load():
         lib.oracle_element_fp64.restype = ctypes.c_double
         lib.oracle_element_fp64.argtypes = [i64, vp, i64, c_int, vp, i64, c_int, vp, i64,
                                             c_int, c_int, i64, i64]
+        dbl, fp = ctypes.c_double, ctypes.c_void_p
+        lib.oracle_gemm_ex.restype = c_int
+        lib.oracle_gemm_ex.argtypes = [i64, i64, i64, vp, i64, c_int, vp, i64, c_int,
+                                       vp, i64, c_int, vp, i64, c_int,
+                                       c_int, c_int, c_int, c_int, dbl, dbl, fp, c_int, c_int]
+        lib.oracle_gemm_ex_sampled.restype = c_int
+        lib.oracle_gemm_ex_sampled.argtypes = [i64, i64, i64, vp, i64, c_int, vp, i64, c_int,
+                                               vp, i64, c_int, i64, vp, vp, vp,
+                                               c_int, c_int, c_int, c_int, dbl, dbl, fp, c_int,
+                                               c_int]
+        lib.oracle_element_ex_fp64.restype = dbl
+        lib.oracle_element_ex_fp64.argtypes = [i64, vp, i64, c_int, vp, i64, c_int,
+                                               vp, i64, c_int, c_int, c_int, dbl, dbl, fp,
+                                               c_int, i64, i64]
+        lib.oracle_activation.restype = dbl
+        lib.oracle_activation.argtypes = [dbl, c_int]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_bf16.restype = ctypes.c_double
@@ -174,3 +196,73 @@ def round_bf16(x: float) -> int:
 
 def round_f32_bits(x: float) -> int:
     return _load().oracle_round_f32_bits(x)
+
+
+def _check_bias(bias, N):
+    if bias is None:
+        return None
+    if bias.dtype != np.float32 or not bias.flags.c_contiguous or bias.size < N:
+        raise TypeError("bias must be a C-contiguous float32 array of at least N values")
+    return bias
+
+
+def gemm_ex(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, D, ldd, layoutD,
+            in_dtype, acc_dtype, out_dtype, satf, alpha=1.0, beta=1.0, bias=None,
+            act=ACT_NONE, nthreads=None):
+    """D = act(alpha * A x B + beta * C + bias) with row/col-major C and D.
+
+    ``bias`` is None or N float32 values (one per column); ``beta == 0``
+    means C is not read.  Only D(i, j) with i < M, j < N is written.
+    """
+    _check_in(A)
+    _check_in(B)
+    _check_out(D, out_dtype)
+    if C is not None:
+        _check_out(C, out_dtype)
+    bias = _check_bias(bias, N)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_gemm_ex(M, N, K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                _ptr(C), ldc, layoutC, _ptr(D), ldd, layoutD,
+                                in_dtype, acc_dtype, out_dtype, int(bool(satf)),
+                                float(alpha), float(beta), _ptr(bias), int(act), nt)
+    if rc != 0:
+        raise ValueError("oracle_gemm_ex rejected its arguments")
+    return D
+
+
+def gemm_ex_sampled(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, rows, cols,
+                    in_dtype, acc_dtype, out_dtype, satf, alpha=1.0, beta=1.0, bias=None,
+                    act=ACT_NONE, nthreads=None):
+    """D(rows[s], cols[s]) of gemm_ex for every s, as a dense out_dtype array."""
+    _check_in(A)
+    _check_in(B)
+    if C is not None:
+        _check_out(C, out_dtype)
+    bias = _check_bias(bias, N)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    out = np.empty(rows.shape, dtype=np.float32 if out_dtype == F32 else np.uint16)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_gemm_ex_sampled(M, N, K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                        _ptr(C), ldc, layoutC, rows.size, _ptr(rows),
+                                        _ptr(cols), _ptr(out), in_dtype, acc_dtype, out_dtype,
+                                        int(bool(satf)), float(alpha), float(beta), _ptr(bias),
+                                        int(act), nt)
+    if rc != 0:
+        raise ValueError("oracle_gemm_ex_sampled rejected its arguments")
+    return out
+
+
+def element_ex_fp64(K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, in_dtype, out_dtype,
+                    alpha, beta, bias, act, i, j):
+    """fp64 value of one gemm_ex element after the activation, before rounding."""
+    return _load().oracle_element_ex_fp64(K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                          _ptr(C), ldc, layoutC, in_dtype, out_dtype,
+                                          float(alpha), float(beta), _ptr(bias), int(act), i, j)
+
+
+def activation(x: float, act: int) -> float:
+    """The oracle's activation function alone (fp64)."""
+    return _load().oracle_activation(x, act)

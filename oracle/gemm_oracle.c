@@ -38,6 +38,10 @@
  *  - C and D are row-major with ldc / ldd; C == NULL means C = 0.
  *  - Rounding is IEEE round-to-nearest-even; subnormals are kept.
  *
+ * The extended form D = act(alpha * (A x B) + beta * C + bias), with C and D
+ * row- or column-major, is at the end of the file with its own sources and
+ * readings.
+ *
  * Parity pins live in the CPU tests: exhaustive fp16 decode against numpy,
  * the RNE encoders against numpy float16/float32 casts and an exact rational
  * encoder, brute force of tiny GEMMs against exact rational sums, the 2x3
@@ -389,3 +393,235 @@ double oracle_element_fp64(int64_t K,
     g.in_dtype = in_dtype; g.out_dtype = out_dtype;
     return dot_plus_c(&g, i, j);
 }
+
+/* ===================================================== extended epilogue
+ *
+ * D = act( alpha * (A x B) + beta * C + bias ), then ONE rounding to the
+ * output dtype, then satf; C and D each row- or column-major.
+ *
+ * Sources: the epilogue-fusion row of "矩阵乘法优化可视化学习文档" section 6
+ * (bias, activation and scale applied before the write-back) and the Triton
+ * notes of section 8 (bias/activation fused at the final store, with the
+ * check that the fused result matches the unfused reference); the
+ * accumulator load/store layouts mem_row_major / mem_col_major of
+ * "CUDA算子优化(5)：WMMA矩阵乘法", section "WMMA API解释" items (3) and (4).
+ *
+ * Readings (the pages name bias, activation and scale but fix none of them):
+ *  - scale is the usual pair alpha (on the product) and beta (on C);
+ *    beta == 0 means C is not read at all;
+ *  - bias is one fp32 value per output column j, added after the scaling;
+ *  - activations: ReLU = max(x, 0) (NaN stays NaN, -0 becomes +0) and GELU in
+ *    its erf form x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with the limits
+ *    GELU(+Inf) = +Inf and GELU(-Inf) = 0;
+ *  - all of it in fp64 before the single final rounding.
+ */
+enum { ORACLE_ACT_NONE = 0, ORACLE_ACT_RELU = 1, ORACLE_ACT_GELU = 2 };
+
+static double act_relu(double x)
+{
+    if (isnan(x))
+        return x;
+    return x > 0.0 ? x : 0.0;
+}
+
+static double act_gelu(double x)
+{
+    if (isnan(x))
+        return x;
+    if (isinf(x))
+        return x > 0.0 ? x : 0.0;
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+static double apply_act(double x, int act)
+{
+    if (act == ORACLE_ACT_RELU)
+        return act_relu(x);
+    if (act == ORACLE_ACT_GELU)
+        return act_gelu(x);
+    return x;
+}
+
+/* C(i,j) / D(i,j): row-major -> [i*ld + j]; col-major -> [j*ld + i]. */
+static int64_t cd_offset(int layout, int64_t ld, int64_t i, int64_t j)
+{
+    return layout == ORACLE_ROW_MAJOR ? i * ld + j : j * ld + i;
+}
+
+typedef struct {
+    job_t base;
+    int layoutC, layoutD;
+    double alpha, beta;
+    const float *bias;
+    int act;
+} job_ex_t;
+
+/* One output element before the final rounding. */
+static double element_ex(const job_ex_t *g, int64_t i, int64_t j)
+{
+    const job_t *b = &g->base;
+    double s = 0.0;
+    for (int64_t k = 0; k < b->K; ++k) {
+        double a = load_in(b->A, b->in_dtype, a_offset(b->layoutA, b->lda, i, k));
+        double bb = load_in(b->B, b->in_dtype, b_offset(b->layoutB, b->ldb, k, j));
+        double prod = a * bb;
+        s = s + prod;
+    }
+    double v = g->alpha * s;
+    if (b->C && g->beta != 0.0)
+        v = v + g->beta * load_out(b->C, b->out_dtype, cd_offset(g->layoutC, b->ldc, i, j));
+    if (g->bias)
+        v = v + (double)g->bias[j];
+    return apply_act(v, g->act);
+}
+
+/* Rows [begin, end): each row's values are computed before any is stored. */
+static void *full_worker_ex(void *arg)
+{
+    const job_ex_t *g = (const job_ex_t *)arg;
+    const job_t *b = &g->base;
+    double *row = (double *)malloc(sizeof(double) * (size_t)(b->N > 0 ? b->N : 1));
+    for (int64_t i = b->begin; i < b->end; ++i) {
+        for (int64_t j = 0; j < b->N; ++j)
+            row[j] = element_ex(g, i, j);
+        for (int64_t j = 0; j < b->N; ++j)
+            store_out(b->D, b->out_dtype, cd_offset(g->layoutD, b->ldd, i, j),
+                      finish_element(row[j], b->out_dtype, b->satf));
+    }
+    free(row);
+    return NULL;
+}
+
+static void *sample_worker_ex(void *arg)
+{
+    const job_ex_t *g = (const job_ex_t *)arg;
+    const job_t *b = &g->base;
+    for (int64_t s = b->begin; s < b->end; ++s) {
+        double v = element_ex(g, b->rows[s], b->cols[s]);
+        store_out(b->out, b->out_dtype, s, finish_element(v, b->out_dtype, b->satf));
+    }
+    return NULL;
+}
+
+static void run_split_ex(job_ex_t *proto, int64_t total, int nthreads, void *(*fn)(void *))
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (total < nthreads)
+        nthreads = total > 0 ? (int)total : 1;
+    pthread_t th[256];
+    job_ex_t jobs[256];
+    int started[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].base.begin = total * t / nthreads;
+        jobs[t].base.end = total * (t + 1) / nthreads;
+        started[t] = (nthreads > 1) && pthread_create(&th[t], NULL, fn, &jobs[t]) == 0;
+        if (!started[t])
+            fn(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t])
+            pthread_join(th[t], NULL);
+}
+
+static int fill_ex(job_ex_t *g, int64_t M, int64_t N, int64_t K,
+                   const void *A, int64_t lda, int layoutA,
+                   const void *B, int64_t ldb, int layoutB,
+                   const void *C, int64_t ldc, int layoutC, int layoutD,
+                   int in_dtype, int out_dtype, int satf,
+                   double alpha, double beta, const float *bias, int act)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (act < ORACLE_ACT_NONE || act > ORACLE_ACT_GELU)
+        return -1;
+    if ((layoutC != ORACLE_ROW_MAJOR && layoutC != ORACLE_COL_MAJOR) ||
+        (layoutD != ORACLE_ROW_MAJOR && layoutD != ORACLE_COL_MAJOR))
+        return -1;
+    memset(g, 0, sizeof *g);
+    job_t *b = &g->base;
+    b->M = M; b->N = N; b->K = K;
+    b->A = A; b->lda = lda; b->layoutA = layoutA;
+    b->B = B; b->ldb = ldb; b->layoutB = layoutB;
+    b->C = C; b->ldc = ldc;
+    b->in_dtype = in_dtype; b->out_dtype = out_dtype; b->satf = satf;
+    g->layoutC = layoutC; g->layoutD = layoutD;
+    g->alpha = alpha; g->beta = beta; g->bias = bias; g->act = act;
+    return 0;
+}
+
+/*
+ * Full extended oracle: writes D(i,j) for i < M, j < N (at cd_offset) and
+ * nothing else.  bias: N fp32 values or NULL.  Returns 0, or -1 for an
+ * argument the definition does not cover.
+ */
+int oracle_gemm_ex(int64_t M, int64_t N, int64_t K,
+                   const void *A, int64_t lda, int layoutA,
+                   const void *B, int64_t ldb, int layoutB,
+                   const void *C, int64_t ldc, int layoutC,
+                   void *D, int64_t ldd, int layoutD,
+                   int in_dtype, int acc_dtype, int out_dtype, int satf,
+                   double alpha, double beta, const float *bias, int act, int nthreads)
+{
+    (void)acc_dtype;
+    job_ex_t g;
+    if (fill_ex(&g, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, layoutD,
+                in_dtype, out_dtype, satf, alpha, beta, bias, act) != 0)
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    g.base.D = D;
+    g.base.ldd = ldd;
+    run_split_ex(&g, M, nthreads, full_worker_ex);
+    return 0;
+}
+
+/* Sampled extended oracle: out[s] = D(rows[s], cols[s]), packed densely. */
+int oracle_gemm_ex_sampled(int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda, int layoutA,
+                           const void *B, int64_t ldb, int layoutB,
+                           const void *C, int64_t ldc, int layoutC,
+                           int64_t nsamples, const int64_t *rows, const int64_t *cols,
+                           void *out,
+                           int in_dtype, int acc_dtype, int out_dtype, int satf,
+                           double alpha, double beta, const float *bias, int act,
+                           int nthreads)
+{
+    (void)acc_dtype;
+    job_ex_t g;
+    if (nsamples < 0 ||
+        fill_ex(&g, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC,
+                ORACLE_ROW_MAJOR, in_dtype, out_dtype, satf, alpha, beta, bias, act) != 0)
+        return -1;
+    for (int64_t s = 0; s < nsamples; ++s)
+        if (rows[s] < 0 || rows[s] >= M || cols[s] < 0 || cols[s] >= N)
+            return -1;
+    g.base.nsamples = nsamples;
+    g.base.rows = rows;
+    g.base.cols = cols;
+    g.base.out = out;
+    run_split_ex(&g, nsamples, nthreads, sample_worker_ex);
+    return 0;
+}
+
+/* The fp64 value of one element after the activation, before the rounding. */
+double oracle_element_ex_fp64(int64_t K,
+                              const void *A, int64_t lda, int layoutA,
+                              const void *B, int64_t ldb, int layoutB,
+                              const void *C, int64_t ldc, int layoutC,
+                              int in_dtype, int out_dtype,
+                              double alpha, double beta, const float *bias, int act,
+                              int64_t i, int64_t j)
+{
+    job_ex_t g;
+    if (fill_ex(&g, 1, 1, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC,
+                ORACLE_ROW_MAJOR, in_dtype, out_dtype, 0, alpha, beta, bias, act) != 0)
+        return NAN;
+    return element_ex(&g, i, j);
+}
+
+/* The activation alone, for the pins. */
+double oracle_activation(double x, int act) { return apply_act(x, act); }
