@@ -24,11 +24,14 @@ __all__ = [
     "GEMM_OK", "GemmError", "LIB_PATH", "library",
     "gemm_run", "gemm_run_config", "gemm_validate", "gemm_status_string",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config",
+    "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU", "GemmEpilogue",
+    "gemm_run_ex", "gemm_run_ex_config", "gemm_validate_ex",
 ]
 
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
 GEMM_F32, GEMM_F16, GEMM_BF16 = 0, 1, 2
 GEMM_OK = 0
+GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU = 0, 1, 2
 STATUS_NAMES = {
     0: "GEMM_OK", -1: "GEMM_ERR_INVALID_DIM", -2: "GEMM_ERR_INVALID_LD",
     -3: "GEMM_ERR_NULL_PTR", -4: "GEMM_ERR_UNSUPPORTED", -5: "GEMM_ERR_INVALID_LAYOUT",
@@ -36,6 +39,20 @@ STATUS_NAMES = {
 }
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libgemm.so")
+
+
+class GemmEpilogue(ctypes.Structure):
+    """gemm_epilogue_t: D = act(alpha * A x B + beta * C + bias), C/D layouts.
+
+    ``bias`` is a device address (int) of N fp32 values, or 0 for none."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("bias", ctypes.c_void_p), ("activation", ctypes.c_int),
+                ("layoutC", ctypes.c_int), ("layoutD", ctypes.c_int)]
+
+    def __init__(self, alpha=1.0, beta=1.0, bias=0, activation=GEMM_ACT_NONE,
+                 layoutC=GEMM_ROW_MAJOR, layoutD=GEMM_ROW_MAJOR):
+        super().__init__(alpha, beta, bias or None, activation, layoutC, layoutD)
+
 
 # Exported symbols and their C signatures (mirrors include/libgemm.h).
 _i64, _int, _vp, _cp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_char_p
@@ -50,6 +67,10 @@ SIGNATURES = {
     "gemm_num_configs": (_int, []),
     "gemm_config_name": (_cp, [_int]),
     "gemm_select_config": (_int, [_i64, _i64, _i64, _int, _int, _int, _int, _int]),
+    "gemm_run_ex": (_int, _GEMM_ARGS[:-1] + [ctypes.POINTER(GemmEpilogue), _vp]),
+    "gemm_run_ex_config": (_int, [_int] + _GEMM_ARGS[:-1] + [ctypes.POINTER(GemmEpilogue), _vp]),
+    "gemm_validate_ex": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _vp, _i64,
+                                _vp, _i64, _int, _int, _int, ctypes.POINTER(GemmEpilogue)]),
 }
 
 
@@ -119,3 +140,32 @@ def gemm_config_name(config_id: int):
 def gemm_select_config(M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype) -> int:
     return library().gemm_select_config(M, N, K, layoutA, layoutB, in_dtype, acc_dtype,
                                         out_dtype)
+
+
+def _epi_ref(epi):
+    return None if epi is None else ctypes.byref(epi)
+
+
+def gemm_run_ex(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                in_dtype, acc_dtype, out_dtype, satf, epi, stream) -> int:
+    """Enqueue D = act(alpha * A x B + beta * C + bias) (``epi``: a GemmEpilogue
+    or None for the plain gemm_run); returns the status code."""
+    return library().gemm_run_ex(M, N, K, A, lda, layoutA, B, ldb, layoutB, C or None, ldc,
+                                 D, ldd, in_dtype, acc_dtype, out_dtype, int(satf),
+                                 _epi_ref(epi), stream or None)
+
+
+def gemm_run_ex_config(config_id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                       in_dtype, acc_dtype, out_dtype, satf, epi, stream) -> int:
+    """gemm_run_ex with the tile-table entry forced; returns the status code."""
+    return library().gemm_run_ex_config(config_id, M, N, K, A, lda, layoutA, B, ldb, layoutB,
+                                        C or None, ldc, D, ldd, in_dtype, acc_dtype, out_dtype,
+                                        int(satf), _epi_ref(epi), stream or None)
+
+
+def gemm_validate_ex(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                     in_dtype, acc_dtype, out_dtype, epi) -> int:
+    """Host-only argument check of gemm_run_ex; returns the status code."""
+    return library().gemm_validate_ex(M, N, K, A or None, lda, layoutA, B or None, ldb,
+                                      layoutB, C or None, ldc, D or None, ldd, in_dtype,
+                                      acc_dtype, out_dtype, _epi_ref(epi))

@@ -80,14 +80,20 @@ bool overlap(const Range &a, const Range &b) {
     return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
 }
 
+const gemm_epilogue_t kPlainEpilogue = {1.0f, 1.0f, nullptr, GEMM_ACT_NONE, GEMM_ROW_MAJOR,
+                                         GEMM_ROW_MAJOR};
+
 int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
              const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, const void *D,
-             int64_t ldd, int in_dtype, int acc_dtype, int out_dtype) {
+             int64_t ldd, int in_dtype, int acc_dtype, int out_dtype,
+             const gemm_epilogue_t *epi) {
+    if (!epi) epi = &kPlainEpilogue;
     const int64_t kMaxDim = 0x7fffffff;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return GEMM_ERR_INVALID_DIM;
-    if ((layoutA != GEMM_ROW_MAJOR && layoutA != GEMM_COL_MAJOR) ||
-        (layoutB != GEMM_ROW_MAJOR && layoutB != GEMM_COL_MAJOR))
+    auto layout_ok = [](int l) { return l == GEMM_ROW_MAJOR || l == GEMM_COL_MAJOR; };
+    if (!layout_ok(layoutA) || !layout_ok(layoutB) || !layout_ok(epi->layoutC) ||
+        !layout_ok(epi->layoutD))
         return GEMM_ERR_INVALID_LAYOUT;
     if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16) return GEMM_ERR_UNSUPPORTED;
     if (acc_dtype == GEMM_F32) {
@@ -98,29 +104,40 @@ int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
     } else {
         return GEMM_ERR_UNSUPPORTED;
     }
+    if (epi->activation != GEMM_ACT_NONE && epi->activation != GEMM_ACT_RELU &&
+        epi->activation != GEMM_ACT_GELU)
+        return GEMM_ERR_UNSUPPORTED;
     const int64_t a_inner = layoutA == GEMM_ROW_MAJOR ? K : M;
     const int64_t a_outer = layoutA == GEMM_ROW_MAJOR ? M : K;
     const int64_t b_inner = layoutB == GEMM_ROW_MAJOR ? N : K;
     const int64_t b_outer = layoutB == GEMM_ROW_MAJOR ? K : N;
+    const int64_t c_inner = epi->layoutC == GEMM_ROW_MAJOR ? N : M;
+    const int64_t c_outer = epi->layoutC == GEMM_ROW_MAJOR ? M : N;
+    const int64_t d_inner = epi->layoutD == GEMM_ROW_MAJOR ? N : M;
+    const int64_t d_outer = epi->layoutD == GEMM_ROW_MAJOR ? M : N;
+    // C is read only when present and beta != 0
+    const bool reads_c = C && epi->beta != 0.0f;
     // leading dimensions: at least one line's worth, and small enough that
     // every element offset fits in 62 bits
     const int64_t kMaxLd = (int64_t)1 << 40;
     if (lda < 1 || lda < a_inner || lda > kMaxLd) return GEMM_ERR_INVALID_LD;
     if (ldb < 1 || ldb < b_inner || ldb > kMaxLd) return GEMM_ERR_INVALID_LD;
-    if (ldd < 1 || ldd < N || ldd > kMaxLd) return GEMM_ERR_INVALID_LD;
-    if (C && (ldc < 1 || ldc < N || ldc > kMaxLd)) return GEMM_ERR_INVALID_LD;
+    if (ldd < 1 || ldd < d_inner || ldd > kMaxLd) return GEMM_ERR_INVALID_LD;
+    if (reads_c && (ldc < 1 || ldc < c_inner || ldc > kMaxLd)) return GEMM_ERR_INVALID_LD;
     if (M == 0 || N == 0) return GEMM_OK;
     if (!D) return GEMM_ERR_NULL_PTR;
     if (K > 0 && (!A || !B)) return GEMM_ERR_NULL_PTR;
 
     const int osz = out_size(out_dtype);
-    const Range rd = extent(D, M, N, ldd, osz);
+    const Range rd = extent(D, d_outer, d_inner, ldd, osz);
     const Range ra = K > 0 ? extent(A, a_outer, a_inner, lda, 2) : extent(A, 0, 0, 1, 2);
     const Range rb = K > 0 ? extent(B, b_outer, b_inner, ldb, 2) : extent(B, 0, 0, 1, 2);
     if (overlap(rd, ra) || overlap(rd, rb)) return GEMM_ERR_ALIASING;
-    if (C) {
-        const bool in_place = (C == D) && (ldc == ldd);
-        if (!in_place && overlap(extent(C, M, N, ldc, osz), rd)) return GEMM_ERR_ALIASING;
+    if (epi->bias && overlap(extent(epi->bias, 1, N, N, 4), rd)) return GEMM_ERR_ALIASING;
+    if (reads_c) {
+        const bool in_place = (C == D) && (ldc == ldd) && (epi->layoutC == epi->layoutD);
+        if (!in_place && overlap(extent(C, c_outer, c_inner, ldc, osz), rd))
+            return GEMM_ERR_ALIASING;
     }
     return GEMM_OK;
 }
@@ -168,12 +185,35 @@ hipError_t workspace(hipStream_t stream, size_t bytes, float **out) {
 int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
         int layoutA, const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
         void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
-        void *stream_handle) {
+        const gemm_epilogue_t *epi_arg, void *stream_handle) {
     int st = validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-                      acc_dtype, out_dtype);
+                      acc_dtype, out_dtype, epi_arg);
     if (st != GEMM_OK) return st;
     if (config_id >= kNumConfigs) return GEMM_ERR_INVALID_CONFIG;
     if (M == 0 || N == 0) return GEMM_OK;
+    const gemm_epilogue_t epi = epi_arg ? *epi_arg : kPlainEpilogue;
+    if (epi.beta == 0.0f) C = nullptr;  // beta == 0: C is not read
+    int layoutC = epi.layoutC;
+    bool bias_rows = false;
+    if (epi.layoutD == GEMM_COL_MAJOR) {
+        // A column-major D is the row-major N x M matrix D^T = B^T x A^T: swap
+        // the operands (each keeps its memory, its layout flag flips), M and
+        // N, and index the bias by row
+        const void *t = A;
+        A = B;
+        B = t;
+        const int64_t tl = lda;
+        lda = ldb;
+        ldb = tl;
+        const int la = layoutA;
+        layoutA = layoutB == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
+        layoutB = la == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
+        const int64_t tm = M;
+        M = N;
+        N = tm;
+        layoutC = layoutC == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
+        bias_rows = true;
+    }
     const int id = config_id >= 0 ? config_id : select_config(M, N, K);
     const Entry &E = kTable[id];
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
@@ -193,6 +233,14 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     p.K = (int)K;
     p.out_dtype = out_dtype;
     p.satf = satf ? 1 : 0;
+    p.c_col = (C && layoutC == GEMM_COL_MAJOR) ? 1 : 0;
+    p.alpha = epi.alpha;
+    p.beta = epi.beta;
+    p.bias = epi.bias;
+    p.bias_rows = bias_rows ? 1 : 0;
+    p.act = epi.activation;
+    p.epi = (epi.alpha != 1.0f || (C && epi.beta != 1.0f) || epi.bias ||
+             epi.activation != GEMM_ACT_NONE || p.c_col) ? 1 : 0;
     // Vector path: 16-byte aligned operands whose extents (rounded up to 16
     // bytes) fit a 32-bit buffer range
     const int64_t a_ext = (layoutA == GEMM_ROW_MAJOR ? (M - 1) * lda + K : (K - 1) * lda + M) * 2;
@@ -204,8 +252,10 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
     const int osz = out_dtype == GEMM_F32 ? 4 : 2;
+    // register epilogue (vector C, D and bias access): aligned row-major C and D
     p.cd_vec = ((uintptr_t)D % (4 * osz) == 0) && (ldd % 4 == 0) &&
-               (!C || (((uintptr_t)C % (4 * osz) == 0) && (ldc % 4 == 0)));
+               (!C || (((uintptr_t)C % (4 * osz) == 0) && (ldc % 4 == 0) && !p.c_col)) &&
+               (!p.bias || p.bias_rows || (uintptr_t)p.bias % 16 == 0);
     p.tiles_m = (int)cdiv(M, E.BM);
     p.tiles_n = (int)cdiv(N, E.BN);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
@@ -254,14 +304,40 @@ int gemm_validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, i
                   const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
                   const void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype) {
     return validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-                    acc_dtype, out_dtype);
+                    acc_dtype, out_dtype, nullptr);
+}
+
+int gemm_validate_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+                     const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
+                     const void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype,
+                     const gemm_epilogue_t *epi) {
+    return validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+                    acc_dtype, out_dtype, epi);
+}
+
+int gemm_run_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+                const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, void *D,
+                int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
+                const gemm_epilogue_t *epi, void *stream) {
+    return run(-1, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+               acc_dtype, out_dtype, satf, epi, stream);
+}
+
+int gemm_run_ex_config(int config_id, int64_t M, int64_t N, int64_t K, const void *A,
+                       int64_t lda, int layoutA, const void *B, int64_t ldb, int layoutB,
+                       const void *C, int64_t ldc, void *D, int64_t ldd, int in_dtype,
+                       int acc_dtype, int out_dtype, int satf, const gemm_epilogue_t *epi,
+                       void *stream) {
+    if (config_id < 0 || config_id >= kNumConfigs) return GEMM_ERR_INVALID_CONFIG;
+    return run(config_id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+               acc_dtype, out_dtype, satf, epi, stream);
 }
 
 int gemm_run(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
              const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, void *D,
              int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf, void *stream) {
     return run(-1, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype, acc_dtype,
-               out_dtype, satf, stream);
+               out_dtype, satf, nullptr, stream);
 }
 
 int gemm_run_config(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
@@ -270,7 +346,7 @@ int gemm_run_config(int config_id, int64_t M, int64_t N, int64_t K, const void *
                     int out_dtype, int satf, void *stream) {
     if (config_id < 0 || config_id >= kNumConfigs) return GEMM_ERR_INVALID_CONFIG;
     return run(config_id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-               acc_dtype, out_dtype, satf, stream);
+               acc_dtype, out_dtype, satf, nullptr, stream);
 }
 
 const char *gemm_status_string(int status) {
@@ -300,7 +376,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
     // validate everything that does not involve pointers or leading dims
     const int st = validate(M, N, K, nullptr, 1 + (layoutA == GEMM_ROW_MAJOR ? K : M), layoutA,
                             nullptr, 1 + (layoutB == GEMM_ROW_MAJOR ? N : K), layoutB, nullptr,
-                            1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype);
+                            1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
     return select_config(M, N, K);
 }

@@ -83,7 +83,17 @@ struct Params {
     int tiles_m, tiles_n;
     int splits;      // K slices (blockIdx.z); 1 = no split
     int k_per_split; // multiple of BK
+    // extended epilogue: v = act(alpha * sum + beta * C + bias).  epi == 0 is
+    // the plain v = sum + C (alpha = beta = 1, no bias, no activation).
+    int epi;
+    float alpha, beta;
+    const float *bias;  // fp32, indexed by column (or by row with bias_rows), or nullptr
+    int bias_rows;
+    int act;            // ACT_*
+    int c_col;          // C column-major: C(i,j) = C[j*ldc + i]
 };
+
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 
 // Block-tile configuration.  MF = 32 selects the 32x32x16 MFMA, 16 the
 // 16x16x32 one.  Waves form a WAVES_M x WAVES_N grid over the block tile.
@@ -425,7 +435,7 @@ __device__ __forceinline__ int acc_col(int lane, int g) {
 
 // ---------------------------------------------------------------- epilogue
 __device__ __forceinline__ float load_c(const Params &p, int64_t i, int64_t j) {
-    const int64_t off = i * p.ldc + j;
+    const int64_t off = p.c_col ? j * p.ldc + i : i * p.ldc + j;
     if (p.out_dtype == DT_F32) return reinterpret_cast<const float *>(p.C)[off];
     const uint16_t h = reinterpret_cast<const uint16_t *>(p.C)[off];
     if (p.out_dtype == DT_F16) return (float)__builtin_bit_cast(_Float16, h);
@@ -440,11 +450,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     return (uint16_t)(u >> 16);
 }
 
-// v = acc (+ C), rounded once to the output dtype OUT, then satf, stored at
-// D(i,j).  OUT is a template argument so the hot epilogue has no dtype branch.
+// ReLU keeps NaN and maps -0 to +0; GELU is x * Phi(x) in its erf form, with
+// its limits at +-Inf.
+__device__ __forceinline__ float activate(float x, int act) {
+    if (act == ACT_RELU) return (x > 0.0f || x != x) ? x : 0.0f;
+    if (act == ACT_GELU) {
+        if (__builtin_isinf(x)) return x > 0.0f ? x : 0.0f;
+        return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    }
+    return x;
+}
+
+// The epilogue of one element before the rounding: sum (+ C), or with the
+// extended epilogue act(alpha * sum + beta * C + bias).
+__device__ __forceinline__ float epilogue_value(const Params &p, int64_t i, int64_t j, float v) {
+    if (!p.epi) return p.C ? v + load_c(p, i, j) : v;
+    v = p.alpha * v;
+    if (p.C) v += p.beta * load_c(p, i, j);
+    if (p.bias) v += p.bias[p.bias_rows ? i : j];
+    return activate(v, p.act);
+}
+
+// The epilogue value of D(i,j), rounded once to the output dtype OUT, then
+// satf, stored at D(i,j).  OUT is a template argument so the hot epilogue has
+// no dtype branch.
 template <int OUT>
 __device__ __forceinline__ void finish_store_t(const Params &p, int64_t i, int64_t j, float v) {
-    if (p.C) v += load_c(p, i, j);
+    v = epilogue_value(p, i, j, v);
     const int64_t off = i * p.ldd + j;
     if constexpr (OUT == DT_F32) {
         if (p.satf) {
@@ -500,11 +532,12 @@ __device__ __forceinline__ float from_out16(uint32_t h) {
 }
 
 // Four consecutive outputs D(i, j..j+3) from fp32 sums v.  OUT < 0: split-K
-// slice, store the raw sums to the workspace.  Otherwise C is added, the
+// slice, store the raw sums to the workspace.  Otherwise the epilogue is
+// applied (EPI: the extended act(alpha*v + beta*C + bias), else v + C), the
 // result rounded once to OUT, satf applied and the group stored.  FULL: the
-// group lies inside M x N and C/D allow 4-element vector access, so no
+// group lies inside M x N and C/D/bias allow 4-element vector access, so no
 // checks; else each element is checked and stored alone.
-template <int OUT, bool FULL>
+template <int OUT, bool FULL, bool EPI>
 __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) {
     const int nval = FULL ? 4 : min(p.N - j, 4);
     if (!FULL && (i >= p.M || nval <= 0)) return;
@@ -517,26 +550,51 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
         }
         return;
     } else {
-        if (p.C) {
-            const int64_t off = (int64_t)i * p.ldc + j;
+        // C(i, j..j+3): one vector load when FULL (then C is row-major)
+        auto c4 = [&]() {
+            f32x4 c;
             if constexpr (OUT == DT_F32) {
-                const float *c = reinterpret_cast<const float *>(p.C) + off;
-                if (FULL) {
-                    v += *reinterpret_cast<const f32x4 *>(c);
-                } else {
-                    for (int e = 0; e < nval; ++e) v[e] += c[e];
-                }
+                const float *cp = reinterpret_cast<const float *>(p.C) + (int64_t)i * p.ldc + j;
+                c = *reinterpret_cast<const f32x4 *>(cp);
             } else {
-                const uint16_t *c = reinterpret_cast<const uint16_t *>(p.C) + off;
+                const uint16_t *cp =
+                    reinterpret_cast<const uint16_t *>(p.C) + (int64_t)i * p.ldc + j;
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(cp);
+                c = f32x4{from_out16<OUT>(lo16(w[0])), from_out16<OUT>(hi16(w[0])),
+                          from_out16<OUT>(lo16(w[1])), from_out16<OUT>(hi16(w[1]))};
+            }
+            return c;
+        };
+        if constexpr (!EPI) {
+            if (p.C) {
                 if (FULL) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(c);
-                    v[0] += from_out16<OUT>(lo16(w[0]));
-                    v[1] += from_out16<OUT>(hi16(w[0]));
-                    v[2] += from_out16<OUT>(lo16(w[1]));
-                    v[3] += from_out16<OUT>(hi16(w[1]));
+                    v += c4();
                 } else {
-                    for (int e = 0; e < nval; ++e) v[e] += from_out16<OUT>(c[e]);
+                    for (int e = 0; e < nval; ++e) v[e] += load_c(p, i, j + e);
                 }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = p.alpha * v[e];
+            if (p.C) {
+                if (FULL) {
+                    v += p.beta * c4();
+                } else {
+                    for (int e = 0; e < nval; ++e) v[e] += p.beta * load_c(p, i, j + e);
+                }
+            }
+            if (p.bias) {
+                if (p.bias_rows) {
+                    v += p.bias[i];
+                } else if (FULL) {
+                    v += *reinterpret_cast<const f32x4 *>(p.bias + j);
+                } else {
+                    for (int e = 0; e < nval; ++e) v[e] += p.bias[j + e];
+                }
+            }
+            if (p.act != ACT_NONE) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = activate(v[e], p.act);
             }
         }
         const int64_t off = (int64_t)i * p.ldd + j;
@@ -828,10 +886,13 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     k_loop<CF, BF, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
 
     // Epilogue.  Each lane owns 4 consecutive columns of one row per register
-    // group.  Interior tiles with vector-friendly C/D finish and store those
-    // straight from registers (C add, convert, satf, one vector store per
-    // group).  Edge tiles, split-K slices and unaligned C/D stage the tile
-    // through LDS and finish it row by row with element checks.
+    // group.  Interior tiles with vector-friendly C/D and the plain epilogue
+    // (+C) finish and store those straight from registers (C add, convert,
+    // satf, one vector store per group).  Everything else -- edge tiles,
+    // split-K slices, unaligned or column-major C, and the extended epilogue
+    // (scale, bias, activation) -- stages the tile through LDS one MF-row block
+    // at a time and finishes it in a loop that is not unrolled, so the
+    // extended arithmetic is instantiated once.
     constexpr int NG = AccT<MF>::N / 4;  // 4-column groups per MFMA tile and lane
     const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.cd_vec && p.splits == 1;
     auto direct = [&](auto out_tag) {
@@ -846,12 +907,12 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                     const int col = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
                     const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    finish4<OUT, true>(p, row, col, v);
+                    finish4<OUT, true, false>(p, row, col, v);
                 });
             });
         });
     };
-    if (full) {
+    if (full && !p.epi) {
         if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
         else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
         else direct(std::integral_constant<int, DT_BF16>{});
@@ -871,27 +932,43 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         float *stage = reinterpret_cast<float *>(smem) + wave * MF * SROW;
         const int row0 = m0 + wm * CF::WTM, col0 = n0 + wn * WTN;
         const int c4 = (lane % LPR) * 4;
-        Unroll<0, TM>::run([&](auto ii) {
-            constexpr int i = decltype(ii)::value;
-            Unroll<0, TN>::run([&](auto jj) {
-                constexpr int j = decltype(jj)::value;
-                Unroll<0, NG>::run([&](auto gg) {
-                    constexpr int g = decltype(gg)::value;
-                    *reinterpret_cast<f32x4 *>(stage + acc_row<MF>(lane) * SROW + j * MF +
-                                               acc_col<MF>(lane, g)) =
-                        f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
+#pragma nounroll
+        for (int i = 0; i < TM; ++i) {
+            // stage row block i (constant accumulator indices in each case)
+            Unroll<0, TM>::run([&](auto ii) {
+                constexpr int ic = decltype(ii)::value;
+                if (ic != i) return;
+                Unroll<0, TN>::run([&](auto jj) {
+                    constexpr int j = decltype(jj)::value;
+                    Unroll<0, NG>::run([&](auto gg) {
+                        constexpr int g = decltype(gg)::value;
+                        *reinterpret_cast<f32x4 *>(stage + acc_row<MF>(lane) * SROW + j * MF +
+                                                   acc_col<MF>(lane, g)) =
+                            f32x4{acc[ic][j][4 * g], acc[ic][j][4 * g + 1],
+                                  acc[ic][j][4 * g + 2], acc[ic][j][4 * g + 3]};
+                    });
                 });
             });
             for (int rr = lane / LPR; rr < MF; rr += RPP) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + rr * SROW + c4);
                 const int gi = row0 + i * MF + rr, gj = col0 + c4;
-                if (p.splits > 1) finish4<-1, false>(p, gi, gj, v);
-                else if (p.out_dtype == DT_F32) finish4<DT_F32, false>(p, gi, gj, v);
-                else if (p.out_dtype == DT_F16) finish4<DT_F16, false>(p, gi, gj, v);
-                else finish4<DT_BF16, false>(p, gi, gj, v);
+                if (p.splits > 1) {
+                    finish4<-1, false, false>(p, gi, gj, v);
+                } else if (full) {  // interior tile, extended epilogue
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, true, true>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true>(p, gi, gj, v);
+                    else finish4<DT_BF16, true, true>(p, gi, gj, v);
+                } else if (p.epi) {
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, true>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true>(p, gi, gj, v);
+                    else finish4<DT_BF16, false, true>(p, gi, gj, v);
+                } else {
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, false>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, false>(p, gi, gj, v);
+                    else finish4<DT_BF16, false, false>(p, gi, gj, v);
+                }
             }
-        });
+        }
     }
 }
 

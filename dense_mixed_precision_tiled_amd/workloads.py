@@ -228,3 +228,83 @@ def w_skinny(values="uniform") -> Problem:
     """16 x 16384 x 16384, fp16 row-major in, fp32 out (sampled check)."""
     return make_problem(16, 16384, 16384, values=values, seed=_seed(6),
                         name="16x16384x16384 fp16->fp32 (%s)" % values)
+
+
+# ------------------------------------------------ extended-epilogue problems
+
+@dataclasses.dataclass
+class EpilogueProblem:
+    """Inputs of one gemm_run_ex call: D = act(alpha * A x B + beta * C + bias)
+    with C and D each row- or column-major.
+
+    C and D buffers have shape (outer, ld): outer = M (row-major) or N
+    (column-major).  ``bias`` is N float32 values or None."""
+    name: str
+    M: int
+    N: int
+    K: int
+    A: np.ndarray
+    lda: int
+    layoutA: int
+    B: np.ndarray
+    ldb: int
+    layoutB: int
+    C: Optional[np.ndarray]
+    ldc: int
+    layoutC: int
+    D: np.ndarray
+    ldd: int
+    layoutD: int
+    in_dtype: int
+    acc_dtype: int
+    out_dtype: int
+    satf: int
+    alpha: float
+    beta: float
+    bias: Optional[np.ndarray]
+    act: int
+    inplace: bool = False
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def make_epilogue_problem(M: int, N: int, K: int, *, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
+                          layoutC=ROW_MAJOR, layoutD=ROW_MAJOR, in_dtype=F16, acc_dtype=F32,
+                          out_dtype=F32, satf=0, values="uniform",
+                          c_values: Optional[str] = "normal", bias_values: Optional[str] = "normal",
+                          alpha=1.0, beta=1.0, act=0, inplace=False, ldc=None, ldd=None,
+                          seed=4321, name="epilogue") -> EpilogueProblem:
+    """Seeded inputs for the extended epilogue (same value recipes as
+    make_problem; the bias is drawn in fp32).  c_values=None: C = NULL."""
+    rng_a = np.random.default_rng(seed)
+    rng_b = np.random.default_rng(seed + 1)
+    rng_c = np.random.default_rng(seed + 2)
+    rng_bias = np.random.default_rng(seed + 5)
+    a_outer, a_inner = (M, K) if layoutA == ROW_MAJOR else (K, M)
+    b_outer, b_inner = (K, N) if layoutB == ROW_MAJOR else (N, K)
+    lda, ldb = max(1, a_inner), max(1, b_inner)
+    A = _operand(rng_a, a_outer, a_inner, lda, in_dtype, values)
+    B = _operand(rng_b, b_outer, b_inner, ldb, in_dtype, values)
+    d_outer, d_inner = (M, N) if layoutD == ROW_MAJOR else (N, M)
+    ldd = max(1, d_inner) + 3 if ldd is None else ldd
+    D = _out_buffer(d_outer, ldd, out_dtype)
+    C = None
+    if inplace:
+        layoutC, ldc = layoutD, ldd
+        cv = _draw(rng_c, (d_outer, d_inner), c_values or "zero")
+        D[:, :d_inner] = cv if out_dtype == F32 else to_bits16(cv, out_dtype)
+        C = D
+    elif c_values is not None:
+        c_outer, c_inner = (M, N) if layoutC == ROW_MAJOR else (N, M)
+        ldc = max(1, c_inner) + 1 if ldc is None else ldc
+        C = _out_buffer(c_outer, ldc, out_dtype)
+        cv = _draw(rng_c, (c_outer, c_inner), c_values)
+        C[:, :c_inner] = cv if out_dtype == F32 else to_bits16(cv, out_dtype)
+    else:
+        ldc = max(1, N if layoutC == ROW_MAJOR else M) if ldc is None else ldc
+    bias = None if bias_values is None else _draw(rng_bias, (N,), bias_values)
+    return EpilogueProblem(name, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC,
+                           D, ldd, layoutD, in_dtype, acc_dtype, out_dtype, satf,
+                           float(alpha), float(beta), bias, int(act), inplace)

@@ -157,6 +157,87 @@ int gemm_validate(int64_t M, int64_t N, int64_t K,
                   const void *D, int64_t ldd,
                   int in_dtype, int acc_dtype, int out_dtype);
 
+/* ===================================================== extended epilogue
+ *
+ * D = act( alpha * (A x B) + beta * C + bias ), rounded once to out_dtype,
+ * then satf; C and D each row- or column-major.
+ *
+ * Sources: "矩阵乘法优化可视化学习文档", section 6 "常用优化方法总表"
+ * (Epilogue fusion row: bias, activation and scale applied before the
+ * write-back) and section 8 (bias/activation fused at the final store, and
+ * the check that the fused result matches the unfused reference); the
+ * accumulator load/store layouts mem_row_major / mem_col_major of
+ * "CUDA算子优化(5)：WMMA矩阵乘法", section "WMMA API解释" items (3) and (4).
+ *
+ * Readings (the pages name bias, activation and scale but fix none of them):
+ *  - scale is the usual pair alpha (on the product) and beta (on C); with
+ *    beta == 0, C is not read (it may hold anything, NaN included);
+ *  - bias holds one fp32 value per column j of D, added after the scaling;
+ *  - GEMM_ACT_RELU is max(x, 0) with NaN kept and -0 -> +0; GEMM_ACT_GELU is
+ *    x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), with GELU(+Inf) = +Inf and
+ *    GELU(-Inf) = 0;
+ *  - everything between the product and the final rounding is fp32.
+ */
+typedef enum {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1,
+    GEMM_ACT_GELU = 2
+} gemm_activation_t;
+
+typedef struct {
+    float alpha;          /* scale of A x B (1.0f: none)                       */
+    float beta;           /* scale of C (1.0f: none; 0.0f: C is not read)      */
+    const float *bias;    /* device pointer to N fp32 values, or NULL          */
+    int activation;       /* gemm_activation_t                                 */
+    int layoutC;          /* gemm_layout_t of C: row-major C(i,j) = C[i*ldc+j],
+                             column-major C(i,j) = C[j*ldc+i]                  */
+    int layoutD;          /* gemm_layout_t of D, same convention               */
+} gemm_epilogue_t;
+
+/*
+ * gemm_run with the extended epilogue.  `epi` == NULL, or
+ * {1, 1, NULL, GEMM_ACT_NONE, GEMM_ROW_MAJOR, GEMM_ROW_MAJOR}, is exactly
+ * gemm_run (bit-identical results).  Other arguments as for gemm_run, except:
+ *   ldc, ldd     >= N for a row-major matrix, >= M for a column-major one.
+ *   C == D       (in place) needs ldc == ldd and layoutC == layoutD.
+ *   bias         N fp32 values on the device; must not overlap D.
+ * Errors, in addition to gemm_run's: an activation outside gemm_activation_t
+ * -> GEMM_ERR_UNSUPPORTED; layoutC / layoutD not a gemm_layout_t ->
+ * GEMM_ERR_INVALID_LAYOUT; bias overlapping D, or C == D with different
+ * layouts or leading dimensions -> GEMM_ERR_ALIASING.
+ *
+ * Speed: a column-major D runs the row-major kernels on D^T = B^T x A^T (the
+ * operands swap roles, no data moves); C in the other layout than D, and
+ * a bias pointer that is not 16-byte aligned, take the element-wise store
+ * path of edge tiles.
+ */
+int gemm_run_ex(int64_t M, int64_t N, int64_t K,
+                const void *A, int64_t lda, int layoutA,
+                const void *B, int64_t ldb, int layoutB,
+                const void *C, int64_t ldc,
+                void *D, int64_t ldd,
+                int in_dtype, int acc_dtype, int out_dtype,
+                int satf, const gemm_epilogue_t *epi, void *stream);
+
+/* gemm_run_ex with the tile-table entry forced (see gemm_run_config). */
+int gemm_run_ex_config(int config_id,
+                       int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, int layoutA,
+                       const void *B, int64_t ldb, int layoutB,
+                       const void *C, int64_t ldc,
+                       void *D, int64_t ldd,
+                       int in_dtype, int acc_dtype, int out_dtype,
+                       int satf, const gemm_epilogue_t *epi, void *stream);
+
+/* Host-only argument check of gemm_run_ex (see gemm_validate). */
+int gemm_validate_ex(int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, int layoutA,
+                     const void *B, int64_t ldb, int layoutB,
+                     const void *C, int64_t ldc,
+                     const void *D, int64_t ldd,
+                     int in_dtype, int acc_dtype, int out_dtype,
+                     const gemm_epilogue_t *epi);
+
 #ifdef __cplusplus
 }
 #endif

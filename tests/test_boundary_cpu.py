@@ -109,6 +109,39 @@ def test_validation_errors(lib):
     assert v(C=D0, ldc=9, ldd=8) == -6       # same base, different ld
 
 
+def vx(M=8, N=6, K=8, C=None, ldc=None, D=D0, ldd=None, alpha=1.0, beta=1.0, bias=0,
+       act=0, lc=R, ld=R, o=F32):
+    ldd = (N if ld == R else M) if ldd is None else ldd
+    ldc = (N if lc == R else M) if ldc is None else ldc
+    epi = lg.GemmEpilogue(alpha, beta, bias, act, lc, ld)
+    return lg.gemm_validate_ex(M, N, K, A0, K, R, B0, N, R, C, ldc, D, ldd, F16, F32, o, epi)
+
+
+def test_validation_ex_ok_cases(lib):
+    assert vx() == 0
+    assert lg.gemm_validate_ex(8, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32,
+                               None) == 0          # NULL epilogue = gemm_run
+    assert vx(act=lg.GEMM_ACT_RELU) == 0 and vx(act=lg.GEMM_ACT_GELU) == 0
+    assert vx(ld=Cm) == 0 and vx(C=C0, lc=Cm) == 0 and vx(C=C0, lc=Cm, ld=Cm) == 0
+    assert vx(bias=0x50000000, alpha=0.5, beta=-2.0) == 0
+    assert vx(C=D0, lc=Cm, ld=Cm) == 0             # in place, column-major
+    assert vx(C=C0, ldc=1, beta=0.0) == 0          # beta == 0: C is not read
+    assert vx(M=8, N=6, ld=Cm, ldd=8) == 0         # column-major D: ldd >= M
+
+
+def test_validation_ex_errors(lib):
+    assert vx(act=3) == -4 and vx(act=-1) == -4
+    assert vx(lc=2) == -5 and vx(ld=7) == -5
+    assert vx(ld=Cm, ldd=7) == -2                  # column-major D needs ldd >= M = 8
+    assert vx(C=C0, lc=Cm, ldc=7) == -2            # column-major C needs ldc >= M
+    assert vx(ld=R, ldd=5) == -2
+    assert vx(bias=D0 + 8) == -6                   # bias inside D
+    assert vx(C=D0, lc=R, ld=Cm, ldc=8, ldd=8) == -6   # same buffer, different layouts
+    st = lg.gemm_run_ex(8, 6, 8, A0, 8, R, B0, 6, R, None, 6, D0, 6, F16, F32, F32, 0,
+                        lg.GemmEpilogue(activation=9), None)
+    assert st == -4                                # rejected before any HIP call
+
+
 def test_run_rejects_before_touching_the_device(lib):
     # argument errors return before any HIP call, so this works without a GPU
     st = lg.gemm_run(-1, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0, None)
