@@ -91,13 +91,24 @@ WORKLOADS = {
                     "A rows x2048, satf=1", "mfma"),
     "wide": ("w_wide", "M=N=16384, K=1024 GEMM, fp16 row-major in, fp32 D", "mfma"),
     "skinny": ("w_skinny", "M=16, N=K=16384 GEMM, fp16 row-major in, fp32 D", "hbm"),
+    # extended epilogue (gemm_run_ex) on the headline shape
+    "4096_f16_bias_gelu": (None, "M=N=K=4096 GEMM, fp16 row-major A and B (uniform[-1,1]), "
+                           "fp32 D = GELU(A x B + bias), bias N(0,1) fp32 per column", "mfma"),
+    "4096_f16_colD": (None, "M=N=K=4096 GEMM, fp16 row-major A and B (uniform[-1,1]), "
+                      "fp32 D column-major, C=0", "mfma"),
 }
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
 def make_workload(W, name):
     gen, desc, bound = WORKLOADS[name]
-    if name.startswith("hgemm"):
+    if name == "4096_f16_bias_gelu":
+        prob = W.make_epilogue_problem(4096, 4096, 4096, values="uniform", c_values=None,
+                                       bias_values="normal", act=2, ldd=4096, seed=20330)
+    elif name == "4096_f16_colD":
+        prob = W.make_epilogue_problem(4096, 4096, 4096, layoutD=1, values="uniform",
+                                       c_values=None, bias_values=None, ldd=4096, seed=20340)
+    elif name.startswith("hgemm"):
         prob = getattr(W, gen)(int(name[-1]), "uniform")
     elif name == "4096_bf16_inplace":
         prob = getattr(W, gen)("normal")
@@ -107,10 +118,12 @@ def make_workload(W, name):
 
 
 def algorithmic_bytes(prob) -> int:
-    """Compulsory HBM bytes: A and B once, C read once (if any), D written once."""
+    """Compulsory HBM bytes: A and B once, C read once (if any), the bias once
+    (if any), D written once."""
     osz = 4 if prob.out_dtype == 0 else 2
     c = prob.M * prob.N * osz if prob.C is not None else 0
-    return 2 * prob.M * prob.K + 2 * prob.K * prob.N + c + prob.M * prob.N * osz
+    bias = 4 * prob.N if getattr(prob, "bias", None) is not None else 0
+    return 2 * prob.M * prob.K + 2 * prob.K * prob.N + c + bias + prob.M * prob.N * osz
 
 
 def main():
@@ -155,10 +168,22 @@ def main():
     else:
         C = None
     stream = torch.cuda.current_stream()
-    call = (prob.M, prob.N, prob.K, A.data_ptr(), prob.lda, prob.layoutA, B.data_ptr(),
-            prob.ldb, prob.layoutB, None if C is None else C.data_ptr(), prob.ldc, D.data_ptr(),
-            prob.ldd, prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf,
-            stream.cuda_stream)
+    epi = getattr(prob, "act", None) is not None  # an extended-epilogue workload
+    if epi:
+        bias = None if prob.bias is None else torch.from_numpy(prob.bias).to(dev)
+        epilogue = lg.GemmEpilogue(prob.alpha, prob.beta, 0 if bias is None else bias.data_ptr(),
+                                   prob.act, prob.layoutC, prob.layoutD)
+        call = (prob.M, prob.N, prob.K, A.data_ptr(), prob.lda, prob.layoutA, B.data_ptr(),
+                prob.ldb, prob.layoutB, None if C is None else C.data_ptr(), prob.ldc,
+                D.data_ptr(), prob.ldd, prob.in_dtype, prob.acc_dtype, prob.out_dtype,
+                prob.satf, epilogue, stream.cuda_stream)
+        run = lg.gemm_run_ex
+    else:
+        call = (prob.M, prob.N, prob.K, A.data_ptr(), prob.lda, prob.layoutA, B.data_ptr(),
+                prob.ldb, prob.layoutB, None if C is None else C.data_ptr(), prob.ldc,
+                D.data_ptr(), prob.ldd, prob.in_dtype, prob.acc_dtype, prob.out_dtype,
+                prob.satf, stream.cuda_stream)
+        run = lg.gemm_run
     cfg = lg.gemm_select_config(prob.M, prob.N, prob.K, prob.layoutA, prob.layoutB,
                                 prob.in_dtype, prob.acc_dtype, prob.out_dtype)
 
@@ -171,7 +196,7 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        st = lg.gemm_run(*call)
+        st = run(*call)
         if st != 0:
             raise lg.GemmError(st)
     torch.cuda.synchronize()
@@ -182,7 +207,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        st = lg.gemm_run(*call)
+        st = run(*call)
         ends[i].record(stream)
         if st != 0:
             raise lg.GemmError(st)
