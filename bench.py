@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--autotune", action="store_true",
+                    help="run gemm_autotune on the workload first (untimed) and time the "
+                         "entry it records")
     ap.add_argument("--workload", default="4096_f16", choices=sorted(WORKLOADS),
                     help="workload to time (default: the headline 4096^3 fp16->fp32)")
     args = ap.parse_args()
@@ -186,6 +189,16 @@ def main():
         run = lg.gemm_run
     cfg = lg.gemm_select_config(prob.M, prob.N, prob.K, prob.layoutA, prob.layoutB,
                                 prob.in_dtype, prob.acc_dtype, prob.out_dtype)
+
+    tuned = None
+    if args.autotune:
+        ex_call = call if epi else call[:-1] + (None, call[-1])
+        t0 = time.perf_counter()
+        st, tuned = lg.gemm_autotune(*ex_call[:-1], 5, ex_call[-1])
+        tune_s = time.perf_counter() - t0
+        if st != 0:
+            raise lg.GemmError(st, "gemm_autotune")
+        cfg = tuned
 
     if args.calibrate_copy:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -249,6 +262,8 @@ def main():
             "workload": desc,
             "M": prob.M, "N": prob.N, "K": prob.K,
             "tile_config": lg.gemm_config_name(cfg),
+            "autotuned": None if tuned is None else {"entry": lg.gemm_config_name(tuned),
+                                                     "tuning_s": round(tune_s, 3)},
         },
         "roofline": dict(roof, **{
             "traffic": traffic,

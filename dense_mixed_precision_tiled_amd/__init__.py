@@ -26,6 +26,7 @@ __all__ = [
     "gemm_num_configs", "gemm_config_name", "gemm_select_config",
     "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU", "GemmEpilogue",
     "gemm_run_ex", "gemm_run_ex_config", "gemm_validate_ex",
+    "gemm_autotune", "gemm_autotune_lookup", "gemm_autotune_clear",
 ]
 
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
@@ -71,6 +72,10 @@ SIGNATURES = {
     "gemm_run_ex_config": (_int, [_int] + _GEMM_ARGS[:-1] + [ctypes.POINTER(GemmEpilogue), _vp]),
     "gemm_validate_ex": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _vp, _i64,
                                 _vp, _i64, _int, _int, _int, ctypes.POINTER(GemmEpilogue)]),
+    "gemm_autotune": (_int, _GEMM_ARGS[:-1] + [ctypes.POINTER(GemmEpilogue), _int,
+                                              ctypes.POINTER(_int), _vp]),
+    "gemm_autotune_lookup": (_int, [_i64, _i64, _i64, _int, _int, _int, _int, _int, _int]),
+    "gemm_autotune_clear": (None, []),
 }
 
 
@@ -169,3 +174,25 @@ def gemm_validate_ex(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
     return library().gemm_validate_ex(M, N, K, A or None, lda, layoutA, B or None, ldb,
                                       layoutB, C or None, ldc, D or None, ldd, in_dtype,
                                       acc_dtype, out_dtype, _epi_ref(epi))
+
+
+def gemm_autotune(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                  in_dtype, acc_dtype, out_dtype, satf, epi, reps, stream):
+    """Time every table entry on this call, record the fastest for the
+    signature; returns (status, chosen entry).  Synchronises the stream."""
+    out = ctypes.c_int(-1)
+    st = library().gemm_autotune(M, N, K, A, lda, layoutA, B, ldb, layoutB, C or None, ldc,
+                                 D, ldd, in_dtype, acc_dtype, out_dtype, int(satf),
+                                 _epi_ref(epi), int(reps), ctypes.byref(out), stream or None)
+    return st, out.value
+
+
+def gemm_autotune_lookup(M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
+                         layoutD=GEMM_ROW_MAJOR) -> int:
+    """The recorded entry for this signature, or -1."""
+    return library().gemm_autotune_lookup(M, N, K, layoutA, layoutB, in_dtype, acc_dtype,
+                                          out_dtype, layoutD)
+
+
+def gemm_autotune_clear() -> None:
+    library().gemm_autotune_clear()

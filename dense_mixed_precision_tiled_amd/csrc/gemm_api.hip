@@ -152,6 +152,35 @@ int select_config(int64_t M, int64_t N, int64_t K) {
     return CFG_SMALL;
 }
 
+// Autotuned choices: problem signature (as the kernels see it, after a
+// column-major D has been turned into D^T) -> table entry.  Process-wide.
+struct TuneKey {
+    int64_t M, N, K;
+    int layoutA, layoutB, in_dtype, acc_dtype, out_dtype, device;
+    bool operator<(const TuneKey &o) const {
+        const int64_t a[9] = {M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype, device};
+        const int64_t b[9] = {o.M, o.N, o.K, o.layoutA, o.layoutB, o.in_dtype, o.acc_dtype,
+                              o.out_dtype, o.device};
+        for (int i = 0; i < 9; ++i)
+            if (a[i] != b[i]) return a[i] < b[i];
+        return false;
+    }
+};
+std::mutex g_tune_mutex;
+std::map<TuneKey, int> g_tune;
+
+int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    return dev;
+}
+
+int tuned_config(const TuneKey &k) {
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    auto it = g_tune.find(k);
+    return it == g_tune.end() ? -1 : it->second;
+}
+
 // Per (device, stream) split-K workspace, grown on demand, held until exit.
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, std::pair<float *, size_t>> g_ws;
@@ -214,7 +243,13 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         layoutC = layoutC == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
         bias_rows = true;
     }
-    const int id = config_id >= 0 ? config_id : select_config(M, N, K);
+    int id = config_id;
+    if (id < 0) {
+        const TuneKey key{M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
+                          current_device()};
+        id = tuned_config(key);
+        if (id < 0) id = select_config(M, N, K);
+    }
     const Entry &E = kTable[id];
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
 
@@ -296,9 +331,107 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     return GEMM_OK;
 }
 
+// The problem signature the kernels see (a column-major D becomes D^T).
+TuneKey tune_key(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB, int in_dtype,
+                 int acc_dtype, int out_dtype, int layoutD) {
+    if (layoutD == GEMM_COL_MAJOR) {
+        const int la = layoutA;
+        layoutA = layoutB == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
+        layoutB = la == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
+        const int64_t t = M;
+        M = N;
+        N = t;
+    }
+    return TuneKey{M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype, current_device()};
+}
+
+int autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+             const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, void *D,
+             int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
+             const gemm_epilogue_t *epi, int reps, int *config_out, void *stream_handle) {
+    int st = validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+                      acc_dtype, out_dtype, epi);
+    if (st != GEMM_OK) return st;
+    const gemm_epilogue_t e = epi ? *epi : kPlainEpilogue;
+    // every candidate runs the call: an in-place update would compound
+    if (C && C == D && e.beta != 0.0f) return GEMM_ERR_ALIASING;
+    if (reps < 1) reps = 1;
+    if (reps > 100) reps = 100;
+    if (M == 0 || N == 0) {
+        if (config_out) *config_out = -1;
+        return GEMM_OK;
+    }
+    hipStream_t stream = static_cast<hipStream_t>(stream_handle);
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return GEMM_ERR_HIP;
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return GEMM_ERR_HIP;
+    }
+    int best = -1;
+    float best_ms = 0.0f;
+    st = GEMM_OK;
+    for (int id = 0; id < kNumConfigs && st == GEMM_OK; ++id) {
+        // one untimed run, then reps timed runs; the minimum counts.  An
+        // entry already 2x slower than the best on its first timed run stops.
+        float cand = -1.0f;
+        for (int r = 0; r <= reps && st == GEMM_OK; ++r) {
+            if (hipEventRecord(ev[0], stream) != hipSuccess) { st = GEMM_ERR_HIP; break; }
+            st = run(id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+                     acc_dtype, out_dtype, satf, epi, stream_handle);
+            if (st != GEMM_OK) break;
+            float ms = 0.0f;
+            if (hipEventRecord(ev[1], stream) != hipSuccess ||
+                hipEventSynchronize(ev[1]) != hipSuccess ||
+                hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
+                st = GEMM_ERR_HIP;
+                break;
+            }
+            if (r == 0) continue;
+            if (cand < 0.0f || ms < cand) cand = ms;
+            if (best >= 0 && cand > 2.0f * best_ms) break;
+        }
+        if (st == GEMM_OK && cand >= 0.0f && (best < 0 || cand < best_ms)) {
+            best = id;
+            best_ms = cand;
+        }
+    }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (st != GEMM_OK) return st;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mutex);
+        g_tune[tune_key(M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
+                        e.layoutD)] = best;
+    }
+    if (config_out) *config_out = best;
+    // leave D holding the chosen entry's result
+    return run(best, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+               acc_dtype, out_dtype, satf, epi, stream_handle);
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+                  const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, void *D,
+                  int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
+                  const gemm_epilogue_t *epi, int reps, int *config_out, void *stream) {
+    return autotune(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
+                    acc_dtype, out_dtype, satf, epi, reps, config_out, stream);
+}
+
+int gemm_autotune_lookup(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB,
+                         int in_dtype, int acc_dtype, int out_dtype, int layoutD) {
+    return tuned_config(tune_key(M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
+                                 layoutD));
+}
+
+void gemm_autotune_clear(void) {
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    g_tune.clear();
+}
 
 int gemm_validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
                   const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,

@@ -240,6 +240,43 @@ int gemm_validate_ex(int64_t M, int64_t N, int64_t K,
                      int in_dtype, int acc_dtype, int out_dtype,
                      const gemm_epilogue_t *epi);
 
+/* ============================================================ autotuning
+ *
+ * Runtime search over the tile-shape table for one problem signature,
+ * cached.  Source: "矩阵乘法优化可视化学习文档", section 6 "常用优化方法总表"
+ * (Autotuning row: the best tile differs with M/N/K, dtype and GPU, and is
+ * found by search) and section 8 (Autotune: one kernel timed over several
+ * block sizes, the fastest kept).
+ *
+ * gemm_autotune runs the call once per table entry (one untimed run, then
+ * `reps` timed runs, clamped to [1, 100]; the minimum counts; an entry more
+ * than 2x slower than the best so far stops early), records the fastest
+ * entry for the signature (M, N, K, layouts, dtypes, current device; a
+ * column-major D is keyed as its transpose, which is what runs), writes it to
+ * *config_out (if not NULL; -1 for an empty problem) and leaves D holding the
+ * chosen entry's result.  From then on gemm_run / gemm_run_ex with that
+ * signature use the recorded entry (gemm_select_config still reports the
+ * static choice).  The call synchronises `stream` (HIP events), so it does
+ * not belong in a timed region or a graph capture.
+ * Arguments and errors as gemm_run_ex, plus: an in-place update (C == D with
+ * beta != 0) -> GEMM_ERR_ALIASING, since every candidate run would apply it.
+ * The cache is process-wide and guarded by a mutex.
+ *
+ * gemm_autotune_lookup: the recorded entry for a signature, or -1.
+ * gemm_autotune_clear: forget every recorded entry.
+ */
+int gemm_autotune(int64_t M, int64_t N, int64_t K,
+                  const void *A, int64_t lda, int layoutA,
+                  const void *B, int64_t ldb, int layoutB,
+                  const void *C, int64_t ldc,
+                  void *D, int64_t ldd,
+                  int in_dtype, int acc_dtype, int out_dtype,
+                  int satf, const gemm_epilogue_t *epi, int reps, int *config_out,
+                  void *stream);
+int gemm_autotune_lookup(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB,
+                         int in_dtype, int acc_dtype, int out_dtype, int layoutD);
+void gemm_autotune_clear(void);
+
 #ifdef __cplusplus
 }
 #endif

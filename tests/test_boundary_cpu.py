@@ -142,6 +142,21 @@ def test_validation_ex_errors(lib):
     assert st == -4                                # rejected before any HIP call
 
 
+def test_autotune_host_side(lib):
+    # argument errors come back before any HIP call; the cache starts empty
+    st, cfg = lg.gemm_autotune(-1, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0,
+                               None, 3, None)
+    assert st == -1 and cfg == -1
+    st, _ = lg.gemm_autotune(8, 8, 8, A0, 8, R, B0, 8, R, D0, 8, D0, 8, F16, F32, F32, 0,
+                             None, 3, None)
+    assert st == -6                          # in place: every candidate would apply it
+    st, cfg = lg.gemm_autotune(0, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0,
+                               None, 3, None)
+    assert st == 0 and cfg == -1             # empty problem: nothing to tune
+    lg.gemm_autotune_clear()
+    assert lg.gemm_autotune_lookup(64, 64, 64, R, R, F16, F32, F32) == -1
+
+
 def test_run_rejects_before_touching_the_device(lib):
     # argument errors return before any HIP call, so this works without a GPU
     st = lg.gemm_run(-1, 8, 8, A0, 8, R, B0, 8, R, None, 8, D0, 8, F16, F32, F32, 0, None)
