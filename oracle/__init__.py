@@ -17,6 +17,8 @@ arrays through ctypes.  Definitions followed (page title, section):
   same page sections 3.2 and 4.2;
 * in-place ``C = A*B + C`` and saturate-to-finite:
   "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释" item (5);
+* int8 x int8 -> int32 (``gemm_i8``): the type lists of
+  "CUDA算子优化(5)：WMMA矩阵乘法" and "深入CUDA Tensor Core与WMMA…" section 2.3;
 * the extended epilogue ``D = act(alpha*(A x B) + beta*C + bias)`` with row- or
   column-major C and D (``gemm_ex``): "矩阵乘法优化可视化学习文档" section 6
   (epilogue fusion) and section 8 (bias/activation at the final store), and the
@@ -43,13 +45,16 @@ LIB = os.path.join(HERE, "liboracle.so")
 F32, F16, BF16 = 0, 1, 2
 ROW_MAJOR, COL_MAJOR = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+I8, I32 = 3, 4
 
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile gemm_oracle.c into liboracle.so with gcc (host only)."""
-    if force or not os.path.exists(LIB):
+    """Compile gemm_oracle.c into liboracle.so with gcc (host only); without
+    force, only when the library is missing or older than the source."""
+    stale = not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC)
+    if force or stale:
         tmp = LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
                "-fPIC", "-shared", "-pthread", SRC, "-o", tmp, "-lm"]
@@ -61,8 +66,7 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            build(force=False)
+        build(force=False)
         lib = ctypes.CDLL(LIB)
         i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.oracle_gemm.restype = c_int
@@ -89,6 +93,12 @@ def _load():
         lib.oracle_element_ex_fp64.argtypes = [i64, vp, i64, c_int, vp, i64, c_int,
                                                vp, i64, c_int, c_int, c_int, dbl, dbl, fp,
                                                c_int, i64, i64]
+        lib.oracle_gemm_i8.restype = c_int
+        lib.oracle_gemm_i8.argtypes = [i64, i64, i64, vp, i64, c_int, vp, i64, c_int,
+                                       vp, i64, c_int, vp, i64, c_int, c_int, c_int]
+        lib.oracle_gemm_i8_sampled.restype = c_int
+        lib.oracle_gemm_i8_sampled.argtypes = [i64, i64, i64, vp, i64, c_int, vp, i64, c_int,
+                                               vp, i64, c_int, i64, vp, vp, vp, c_int, c_int]
         lib.oracle_activation.restype = dbl
         lib.oracle_activation.argtypes = [dbl, c_int]
         lib.oracle_decode_f16.restype = ctypes.c_double
@@ -266,3 +276,50 @@ def element_ex_fp64(K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, in_dty
 def activation(x: float, act: int) -> float:
     """The oracle's activation function alone (fp64)."""
     return _load().oracle_activation(x, act)
+
+
+def _check_i8(a):
+    if a.dtype != np.int8 or not a.flags.c_contiguous:
+        raise TypeError("A/B must be C-contiguous int8 arrays")
+
+
+def _check_i32(a):
+    if a.dtype != np.int32 or not a.flags.c_contiguous:
+        raise TypeError("C/D must be C-contiguous int32 arrays")
+
+
+def gemm_i8(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, D, ldd, layoutD,
+            satf, nthreads=None):
+    """D = to_int32(A x B + C) for int8 A, B and int32 C, D: the exact sum,
+    wrapped modulo 2^32, or clamped to the int32 range with satf."""
+    _check_i8(A)
+    _check_i8(B)
+    _check_i32(D)
+    if C is not None:
+        _check_i32(C)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_gemm_i8(M, N, K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                _ptr(C), ldc, layoutC, _ptr(D), ldd, layoutD,
+                                int(bool(satf)), nt)
+    if rc != 0:
+        raise ValueError("oracle_gemm_i8 rejected its arguments")
+    return D
+
+
+def gemm_i8_sampled(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, rows, cols,
+                    satf, nthreads=None):
+    """D(rows[s], cols[s]) of gemm_i8 for every s (int32)."""
+    _check_i8(A)
+    _check_i8(B)
+    if C is not None:
+        _check_i32(C)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(rows.shape, dtype=np.int32)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_gemm_i8_sampled(M, N, K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
+                                        _ptr(C), ldc, layoutC, rows.size, _ptr(rows),
+                                        _ptr(cols), _ptr(out), int(bool(satf)), nt)
+    if rc != 0:
+        raise ValueError("oracle_gemm_i8_sampled rejected its arguments")
+    return out

@@ -625,3 +625,152 @@ double oracle_element_ex_fp64(int64_t K,
 
 /* The activation alone, for the pins. */
 double oracle_activation(double x, int act) { return apply_act(x, act); }
+
+/* ============================================================ int8 -> int32
+ *
+ * D(i,j) = to_int32( sum_k A(i,k) * B(k,j) + C(i,j) ), A and B int8 (two's
+ * complement), C and D int32, each of C and D row- or column-major.
+ *
+ * Sources: the fragment type lists of "CUDA算子优化(5)：WMMA矩阵乘法" (A/B of
+ * char / unsigned char with an int accumulator) and of "深入CUDA Tensor Core与
+ * WMMA…" section 2.3 (INT8 on the matrix units); the sum itself is the element
+ * definition of "矩阵乘法优化可视化学习文档" section 1.
+ *
+ * Readings: the sum is exact (int64 here: |a*b| <= 2^14, so any K < 2^49
+ * fits); to_int32 wraps modulo 2^32 (two's complement), or with satf clamps
+ * the exact value to [-2^31, 2^31 - 1] (the integer form of saturating to
+ * the largest finite value); C == NULL means 0.
+ */
+static int32_t to_int32(int64_t v, int satf)
+{
+    if (satf) {
+        if (v > INT32_MAX)
+            return INT32_MAX;
+        if (v < INT32_MIN)
+            return INT32_MIN;
+        return (int32_t)v;
+    }
+    return (int32_t)(uint32_t)(uint64_t)v; /* modulo 2^32 */
+}
+
+typedef struct {
+    int64_t M, N, K;
+    const int8_t *A; int64_t lda; int layoutA;
+    const int8_t *B; int64_t ldb; int layoutB;
+    const int32_t *C; int64_t ldc; int layoutC;
+    int32_t *D; int64_t ldd; int layoutD;
+    int satf;
+    const int64_t *rows, *cols;
+    int32_t *out;
+    int64_t begin, end;
+} job_i8_t;
+
+static int64_t element_i8(const job_i8_t *g, int64_t i, int64_t j)
+{
+    int64_t s = 0;
+    for (int64_t k = 0; k < g->K; ++k)
+        s += (int64_t)g->A[a_offset(g->layoutA, g->lda, i, k)] *
+             (int64_t)g->B[b_offset(g->layoutB, g->ldb, k, j)];
+    if (g->C)
+        s += g->C[cd_offset(g->layoutC, g->ldc, i, j)];
+    return s;
+}
+
+static void *full_worker_i8(void *arg)
+{
+    const job_i8_t *g = (const job_i8_t *)arg;
+    int64_t *row = (int64_t *)malloc(sizeof(int64_t) * (size_t)(g->N > 0 ? g->N : 1));
+    for (int64_t i = g->begin; i < g->end; ++i) {
+        for (int64_t j = 0; j < g->N; ++j)
+            row[j] = element_i8(g, i, j);
+        for (int64_t j = 0; j < g->N; ++j)
+            g->D[cd_offset(g->layoutD, g->ldd, i, j)] = to_int32(row[j], g->satf);
+    }
+    free(row);
+    return NULL;
+}
+
+static void *sample_worker_i8(void *arg)
+{
+    const job_i8_t *g = (const job_i8_t *)arg;
+    for (int64_t s = g->begin; s < g->end; ++s)
+        g->out[s] = to_int32(element_i8(g, g->rows[s], g->cols[s]), g->satf);
+    return NULL;
+}
+
+static void run_split_i8(job_i8_t *proto, int64_t total, int nthreads, void *(*fn)(void *))
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (total < nthreads)
+        nthreads = total > 0 ? (int)total : 1;
+    pthread_t th[256];
+    job_i8_t jobs[256];
+    int started[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].begin = total * t / nthreads;
+        jobs[t].end = total * (t + 1) / nthreads;
+        started[t] = (nthreads > 1) && pthread_create(&th[t], NULL, fn, &jobs[t]) == 0;
+        if (!started[t])
+            fn(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t])
+            pthread_join(th[t], NULL);
+}
+
+/* Full int8 oracle: writes D(i,j) for i < M, j < N and nothing else. */
+int oracle_gemm_i8(int64_t M, int64_t N, int64_t K,
+                   const int8_t *A, int64_t lda, int layoutA,
+                   const int8_t *B, int64_t ldb, int layoutB,
+                   const int32_t *C, int64_t ldc, int layoutC,
+                   int32_t *D, int64_t ldd, int layoutD, int satf, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if ((layoutC != ORACLE_ROW_MAJOR && layoutC != ORACLE_COL_MAJOR) ||
+        (layoutD != ORACLE_ROW_MAJOR && layoutD != ORACLE_COL_MAJOR))
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    job_i8_t g;
+    memset(&g, 0, sizeof g);
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.layoutA = layoutA;
+    g.B = B; g.ldb = ldb; g.layoutB = layoutB;
+    g.C = C; g.ldc = ldc; g.layoutC = layoutC;
+    g.D = D; g.ldd = ldd; g.layoutD = layoutD;
+    g.satf = satf;
+    run_split_i8(&g, M, nthreads, full_worker_i8);
+    return 0;
+}
+
+/* Sampled int8 oracle: out[s] = D(rows[s], cols[s]). */
+int oracle_gemm_i8_sampled(int64_t M, int64_t N, int64_t K,
+                           const int8_t *A, int64_t lda, int layoutA,
+                           const int8_t *B, int64_t ldb, int layoutB,
+                           const int32_t *C, int64_t ldc, int layoutC,
+                           int64_t nsamples, const int64_t *rows, const int64_t *cols,
+                           int32_t *out, int satf, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || nsamples < 0)
+        return -1;
+    if (layoutC != ORACLE_ROW_MAJOR && layoutC != ORACLE_COL_MAJOR)
+        return -1;
+    for (int64_t s = 0; s < nsamples; ++s)
+        if (rows[s] < 0 || rows[s] >= M || cols[s] < 0 || cols[s] >= N)
+            return -1;
+    job_i8_t g;
+    memset(&g, 0, sizeof g);
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.layoutA = layoutA;
+    g.B = B; g.ldb = ldb; g.layoutB = layoutB;
+    g.C = C; g.ldc = ldc; g.layoutC = layoutC;
+    g.satf = satf;
+    g.rows = rows; g.cols = cols; g.out = out;
+    run_split_i8(&g, nsamples, nthreads, sample_worker_i8);
+    return 0;
+}
