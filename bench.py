@@ -96,7 +96,11 @@ WORKLOADS = {
                            "fp32 D = GELU(A x B + bias), bias N(0,1) fp32 per column", "mfma"),
     "4096_f16_colD": (None, "M=N=K=4096 GEMM, fp16 row-major A and B (uniform[-1,1]), "
                       "fp32 D column-major, C=0", "mfma"),
+    # int8 x int8 -> int32
+    "4096_i8": (None, "M=N=K=4096 GEMM, int8 A row-major and B column-major (uniform over "
+                "[-128,127]), int32 accumulate and D, C=0", "mfma_i8"),
 }
+PEAK_I8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
@@ -105,6 +109,8 @@ def make_workload(W, name):
     if name == "4096_f16_bias_gelu":
         prob = W.make_epilogue_problem(4096, 4096, 4096, values="uniform", c_values=None,
                                        bias_values="normal", act=2, ldd=4096, seed=20330)
+    elif name == "4096_i8":
+        prob = W.make_int8_problem(4096, 4096, 4096, values="full", c_values=None, seed=20350)
     elif name == "4096_f16_colD":
         prob = W.make_epilogue_problem(4096, 4096, 4096, layoutD=1, values="uniform",
                                        c_values=None, bias_values=None, ldd=4096, seed=20340)
@@ -161,13 +167,14 @@ def main():
 
     prob, desc, bound = make_workload(W, args.workload)
     dev = torch.device("cuda:0")
-    A = torch.from_numpy(prob.A.view(np.int16)).to(dev)
-    B = torch.from_numpy(prob.B.view(np.int16)).to(dev)
-    D = torch.from_numpy(prob.D.view(np.int16) if prob.D.dtype == np.uint16 else prob.D).to(dev)
+    def to_dev(x):  # 16-bit patterns travel as int16; everything else as is
+        return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
+
+    A, B, D = to_dev(prob.A), to_dev(prob.B), to_dev(prob.D)
     if prob.inplace:
         C = D
     elif prob.C is not None:
-        C = torch.from_numpy(prob.C.view(np.int16) if prob.C.dtype == np.uint16 else prob.C).to(dev)
+        C = to_dev(prob.C)
     else:
         C = None
     stream = torch.cuda.current_stream()
@@ -235,7 +242,10 @@ def main():
     achieved = flop / (mean_ms * 1e-3) / 1e12
     traffic = load_traffic() if args.workload == "4096_f16" else None
     nbytes = algorithmic_bytes(prob)
-    if bound == "hbm":
+    if bound == "mfma_i8":
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4)}
+    elif bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(nbytes / (mean_ms * 1e-3) / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(nbytes / (mean_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
@@ -245,10 +255,12 @@ def main():
 
     out = {
         "metric": METRIC if args.workload == "4096_f16" else
-        "GEMM TFLOP/s (2MNK/t), workload %s" % args.workload,
+        "GEMM %s (2MNK/t), workload %s" % ("TOP/s" if prob.in_dtype == 3 else "TFLOP/s",
+                                           args.workload),
         "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "unit": "TOP/s" if prob.in_dtype == 3 else "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / (PEAK_I8_TOPS if prob.in_dtype == 3
+                                               else PEAK_TFLOPS), 2),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -256,7 +268,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if prob.in_dtype == 2 else "f16",
+        "dtype": {2: "bf16", 3: "i8"}.get(prob.in_dtype, "f16"),
         "data": "synthetic",
         "config": {
             "workload": desc,

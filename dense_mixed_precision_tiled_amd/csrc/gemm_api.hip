@@ -15,13 +15,25 @@ using namespace libgemm;
 
 namespace libgemm {
 // Split-K reduction: D(i,j) = finish(sum over slices in slice order + C).
+// int32 outputs: the slices hold int32 bit patterns, summed in 64 bits.
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(Params p) {
     const int64_t total = (int64_t)p.M * p.N;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
-        float s = 0.0f;
-        for (int z = 0; z < p.splits; ++z) s += p.ws[z * total + idx];
-        finish_store(p, idx / p.N, idx % p.N, s);
+        const int64_t i = idx / p.N, j = idx % p.N;
+        if (p.out_dtype == DT_I32) {
+            const int32_t *w = reinterpret_cast<const int32_t *>(p.ws);
+            int64_t s = 0;
+            for (int z = 0; z < p.splits; ++z) s += w[z * total + idx];
+            if (p.C)
+                s += reinterpret_cast<const int32_t *>(p.C)[p.c_col ? j * p.ldc + i
+                                                                    : i * p.ldc + j];
+            reinterpret_cast<int32_t *>(p.D)[i * p.ldd + j] = to_int32(s, p.satf);
+        } else {
+            float s = 0.0f;
+            for (int z = 0; z < p.splits; ++z) s += p.ws[z * total + idx];
+            finish_store(p, i, j, s);
+        }
     }
 }
 
@@ -33,29 +45,42 @@ struct Entry {
     const char *name;
     int BM, BN, BK;
     int split_k;  // 1: this entry may split K across workgroups
+    int klass;    // input class: 0 = fp16/bf16, 1 = int8
     launch_fn launch;
 };
 
 const Entry kTable[] = {
-    {"large_256x256x64_w2x2_mfma32x32x16", CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, 0,
+    {"large_256x256x64_w2x2_mfma32x32x16", CfgLarge::BM, CfgLarge::BN, CfgLarge::BK, 0, 0,
      launch_large},
-    {"medium_128x128x64_w2x2_mfma32x32x16", CfgMedium::BM, CfgMedium::BN, CfgMedium::BK, 0,
+    {"medium_128x128x64_w2x2_mfma32x32x16", CfgMedium::BM, CfgMedium::BN, CfgMedium::BK, 0, 0,
      launch_medium},
-    {"small_64x64x64_w2x2_mfma32x32x16", CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, 0,
+    {"small_64x64x64_w2x2_mfma32x32x16", CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, 0, 0,
      launch_small},
     {"skinny_16x128x128_w1x4_mfma16x16x32_splitk", CfgSkinny::BM, CfgSkinny::BN, CfgSkinny::BK, 1,
-     launch_skinny},
-    {"large8_256x256x64_w2x4_mfma32x32x16", CfgLarge8::BM, CfgLarge8::BN, CfgLarge8::BK, 0,
+     0, launch_skinny},
+    {"large8_256x256x64_w2x4_mfma32x32x16", CfgLarge8::BM, CfgLarge8::BN, CfgLarge8::BK, 0, 0,
      launch_large8},
+    {"i8_large8_256x256x128_w2x4_mfma32x32x32", CfgLarge8I8::BM, CfgLarge8I8::BN, CfgLarge8I8::BK,
+     0, 1, launch_large8_i8},
+    {"i8_medium_128x128x128_w2x2_mfma32x32x32", CfgMediumI8::BM, CfgMediumI8::BN, CfgMediumI8::BK,
+     0, 1, launch_medium_i8},
+    {"i8_small_64x64x128_w2x2_mfma32x32x32", CfgSmallI8::BM, CfgSmallI8::BN, CfgSmallI8::BK, 0, 1,
+     launch_small_i8},
+    {"i8_skinny_16x128x256_w1x4_mfma16x16x64_splitk", CfgSkinnyI8::BM, CfgSkinnyI8::BN,
+     CfgSkinnyI8::BK, 1, 1, launch_skinny_i8},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
-enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4 };
+enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
+       CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8 };
+
+int input_class(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : 0; }
+int in_size(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : 2; }
 
 constexpr int kCUs = 256;  // MI355X compute units
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int out_size(int dt) { return dt == GEMM_F32 ? 4 : 2; }
+int out_size(int dt) { return (dt == GEMM_F32 || dt == GEMM_I32) ? 4 : 2; }
 
 // Byte range [lo, hi) of a matrix with `outer` lines of `inner` elements at
 // stride ld; empty when either count is zero.
@@ -86,17 +111,29 @@ const gemm_epilogue_t kPlainEpilogue = {1.0f, 1.0f, nullptr, GEMM_ACT_NONE, GEMM
 int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
              const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, const void *D,
              int64_t ldd, int in_dtype, int acc_dtype, int out_dtype,
-             const gemm_epilogue_t *epi) {
+             const gemm_epilogue_t *epi, int satf_arg) {
     if (!epi) epi = &kPlainEpilogue;
     const int64_t kMaxDim = 0x7fffffff;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return GEMM_ERR_INVALID_DIM;
+    if (in_dtype == GEMM_I8 && acc_dtype == GEMM_I32 && out_dtype == GEMM_I32 && satf_arg &&
+        K >= ((int64_t)1 << 17))
+        return GEMM_ERR_UNSUPPORTED;
     auto layout_ok = [](int l) { return l == GEMM_ROW_MAJOR || l == GEMM_COL_MAJOR; };
     if (!layout_ok(layoutA) || !layout_ok(layoutB) || !layout_ok(epi->layoutC) ||
         !layout_ok(epi->layoutD))
         return GEMM_ERR_INVALID_LAYOUT;
-    if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16) return GEMM_ERR_UNSUPPORTED;
-    if (acc_dtype == GEMM_F32) {
+    if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16 && in_dtype != GEMM_I8)
+        return GEMM_ERR_UNSUPPORTED;
+    if (in_dtype == GEMM_I8) {
+        // int8 x int8 -> int32: the plain epilogue only (C/D layouts allowed);
+        // satf clamps the exact sum, which the int32 accumulator holds only
+        // for K < 2^17 (|a*b| <= 2^14)
+        if (acc_dtype != GEMM_I32 || out_dtype != GEMM_I32) return GEMM_ERR_UNSUPPORTED;
+        if (epi->alpha != 1.0f || (C && epi->beta != 1.0f && epi->beta != 0.0f) || epi->bias ||
+            epi->activation != GEMM_ACT_NONE)
+            return GEMM_ERR_UNSUPPORTED;
+    } else if (acc_dtype == GEMM_F32) {
         if (out_dtype != GEMM_F32 && out_dtype != GEMM_F16 && out_dtype != GEMM_BF16)
             return GEMM_ERR_UNSUPPORTED;
     } else if (acc_dtype == GEMM_F16) {
@@ -130,8 +167,9 @@ int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
 
     const int osz = out_size(out_dtype);
     const Range rd = extent(D, d_outer, d_inner, ldd, osz);
-    const Range ra = K > 0 ? extent(A, a_outer, a_inner, lda, 2) : extent(A, 0, 0, 1, 2);
-    const Range rb = K > 0 ? extent(B, b_outer, b_inner, ldb, 2) : extent(B, 0, 0, 1, 2);
+    const int isz = in_size(in_dtype);
+    const Range ra = K > 0 ? extent(A, a_outer, a_inner, lda, isz) : extent(A, 0, 0, 1, isz);
+    const Range rb = K > 0 ? extent(B, b_outer, b_inner, ldb, isz) : extent(B, 0, 0, 1, isz);
     if (overlap(rd, ra) || overlap(rd, rb)) return GEMM_ERR_ALIASING;
     if (epi->bias && overlap(extent(epi->bias, 1, N, N, 4), rd)) return GEMM_ERR_ALIASING;
     if (reads_c) {
@@ -142,14 +180,15 @@ int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
     return GEMM_OK;
 }
 
-int select_config(int64_t M, int64_t N, int64_t K) {
+int select_config(int64_t M, int64_t N, int64_t K, int klass) {
     (void)K;
-    if (M <= CfgSkinny::BM) return CFG_SKINNY;
+    const bool i8 = klass == 1;
+    if (M <= CfgSkinny::BM) return i8 ? CFG_I8_SKINNY : CFG_SKINNY;
     const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
-    if (t_large >= 3 * kCUs / 4) return CFG_LARGE8;
+    if (t_large >= 3 * kCUs / 4) return i8 ? CFG_I8_LARGE8 : CFG_LARGE8;
     const int64_t t_medium = cdiv(M, CfgMedium::BM) * cdiv(N, CfgMedium::BN);
-    if (t_medium >= kCUs / 2) return CFG_MEDIUM;
-    return CFG_SMALL;
+    if (t_medium >= kCUs / 2) return i8 ? CFG_I8_MEDIUM : CFG_MEDIUM;
+    return i8 ? CFG_I8_SMALL : CFG_SMALL;
 }
 
 // Autotuned choices: problem signature (as the kernels see it, after a
@@ -216,9 +255,11 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
         const gemm_epilogue_t *epi_arg, void *stream_handle) {
     int st = validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-                      acc_dtype, out_dtype, epi_arg);
+                      acc_dtype, out_dtype, epi_arg, satf);
     if (st != GEMM_OK) return st;
-    if (config_id >= kNumConfigs) return GEMM_ERR_INVALID_CONFIG;
+    const int klass = input_class(in_dtype);
+    if (config_id >= kNumConfigs || (config_id >= 0 && kTable[config_id].klass != klass))
+        return GEMM_ERR_INVALID_CONFIG;
     if (M == 0 || N == 0) return GEMM_OK;
     const gemm_epilogue_t epi = epi_arg ? *epi_arg : kPlainEpilogue;
     if (epi.beta == 0.0f) C = nullptr;  // beta == 0: C is not read
@@ -248,7 +289,7 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         const TuneKey key{M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
                           current_device()};
         id = tuned_config(key);
-        if (id < 0) id = select_config(M, N, K);
+        if (id < 0) id = select_config(M, N, K, klass);
     }
     const Entry &E = kTable[id];
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
@@ -276,17 +317,22 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     p.act = epi.activation;
     p.epi = (epi.alpha != 1.0f || (C && epi.beta != 1.0f) || epi.bias ||
              epi.activation != GEMM_ACT_NONE || p.c_col) ? 1 : 0;
-    // Vector path: 16-byte aligned operands whose extents (rounded up to 16
-    // bytes) fit a 32-bit buffer range
-    const int64_t a_ext = (layoutA == GEMM_ROW_MAJOR ? (M - 1) * lda + K : (K - 1) * lda + M) * 2;
-    const int64_t b_ext = (layoutB == GEMM_ROW_MAJOR ? (K - 1) * ldb + N : (N - 1) * ldb + K) * 2;
+    // Vector path: 16-byte aligned operands (lines a multiple of 16 bytes)
+    // whose extents, rounded up to 16 bytes, fit a 32-bit buffer range; int8
+    // operands must also be K-contiguous (A row-major, B column-major)
+    const int isz = in_size(in_dtype);
+    const int64_t a_ext =
+        (layoutA == GEMM_ROW_MAJOR ? (M - 1) * lda + K : (K - 1) * lda + M) * isz;
+    const int64_t b_ext =
+        (layoutB == GEMM_ROW_MAJOR ? (K - 1) * ldb + N : (N - 1) * ldb + K) * isz;
     const int64_t a_rng = (a_ext + 15) & ~(int64_t)15, b_rng = (b_ext + 15) & ~(int64_t)15;
     p.vec_ok = K > 0 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
-               (lda % 8 == 0) && (ldb % 8 == 0) && a_rng < ((int64_t)1 << 32) - 16 &&
-               b_rng < ((int64_t)1 << 32) - 16;
+               ((lda * isz) % 16 == 0) && ((ldb * isz) % 16 == 0) &&
+               a_rng < ((int64_t)1 << 32) - 16 && b_rng < ((int64_t)1 << 32) - 16 &&
+               (isz == 2 || (layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR));
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
-    const int osz = out_dtype == GEMM_F32 ? 4 : 2;
+    const int osz = out_size(out_dtype);
     // register epilogue (vector C, D and bias access): aligned row-major C and D
     p.cd_vec = ((uintptr_t)D % (4 * osz) == 0) && (ldd % 4 == 0) &&
                (!C || (((uintptr_t)C % (4 * osz) == 0) && (ldc % 4 == 0) && !p.c_col)) &&
@@ -350,7 +396,7 @@ int autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
              int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
              const gemm_epilogue_t *epi, int reps, int *config_out, void *stream_handle) {
     int st = validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-                      acc_dtype, out_dtype, epi);
+                      acc_dtype, out_dtype, epi, satf);
     if (st != GEMM_OK) return st;
     const gemm_epilogue_t e = epi ? *epi : kPlainEpilogue;
     // every candidate runs the call: an in-place update would compound
@@ -372,6 +418,7 @@ int autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
     float best_ms = 0.0f;
     st = GEMM_OK;
     for (int id = 0; id < kNumConfigs && st == GEMM_OK; ++id) {
+        if (kTable[id].klass != input_class(in_dtype)) continue;
         // one untimed run, then reps timed runs; the minimum counts.  An
         // entry already 2x slower than the best on its first timed run stops.
         float cand = -1.0f;
@@ -437,7 +484,7 @@ int gemm_validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, i
                   const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
                   const void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype) {
     return validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-                    acc_dtype, out_dtype, nullptr);
+                    acc_dtype, out_dtype, nullptr, 0);
 }
 
 int gemm_validate_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
@@ -445,7 +492,7 @@ int gemm_validate_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
                      const void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype,
                      const gemm_epilogue_t *epi) {
     return validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
-                    acc_dtype, out_dtype, epi);
+                    acc_dtype, out_dtype, epi, 0);
 }
 
 int gemm_run_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
@@ -509,9 +556,9 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
     // validate everything that does not involve pointers or leading dims
     const int st = validate(M, N, K, nullptr, 1 + (layoutA == GEMM_ROW_MAJOR ? K : M), layoutA,
                             nullptr, 1 + (layoutB == GEMM_ROW_MAJOR ? N : K), layoutB, nullptr,
-                            1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr);
+                            1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr, 0);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
-    return select_config(M, N, K);
+    return select_config(M, N, K, input_class(in_dtype));
 }
 
 }  // extern "C"

@@ -22,6 +22,13 @@ using CfgSmall = TileCfg<64, 64, 64, 2, 2, 32, 4>;
 // MFMA, split-K so enough workgroups stream B.
 using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16, 1>;
 
+// int8 entries: the same tiles in bytes (BK = 128 int8 values per LDS row of
+// 128 bytes), v_mfma_i32_32x32x32_i8 / v_mfma_i32_16x16x64_i8.
+using CfgLarge8I8 = TileCfg<256, 256, 128, 2, 4, 32, 4, 1>;
+using CfgMediumI8 = TileCfg<128, 128, 128, 2, 2, 32, 4, 1>;
+using CfgSmallI8 = TileCfg<64, 64, 128, 2, 2, 32, 4, 1>;
+using CfgSkinnyI8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 1>;
+
 typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
                                 dim3 grid, hipStream_t stream);
 
@@ -41,29 +48,41 @@ LIBGEMM_DECLARE_LAUNCH(small)
 LIBGEMM_DECLARE_LAUNCH(skinny)
 #undef LIBGEMM_DECLARE_LAUNCH
 
-template <class CF, bool BF, bool AKC, bool BKC>
+// one translation unit per int8 entry: kernels_<entry>_i8.hip (the bf flag of
+// launch_fn is ignored)
+hipError_t launch_large8_i8(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_medium_i8(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_small_i8(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_skinny_i8(const Params &, int, int, int, dim3, hipStream_t);
+
+template <class CF, int IT, bool AKC, bool BKC>
 hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
     // the K loop masks k >= kend only when some slice ends inside a K-tile
     const bool ragged = (p.K % CF::BK) != 0 || (p.k_per_split % CF::BK) != 0;
-    if (!p.vec_ok)
-        hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC, false, false>), grid,
+    // int8 vector loads need both operands K-contiguous (the host's vec_ok
+    // says so); other int8 layouts take the element-wise loads
+    constexpr bool can_vec = CF::ES == 2 || (AKC && BKC);
+    if (!can_vec || !p.vec_ok)
+        hipLaunchKernelGGL((gemm_mfma_kernel<CF, IT, AKC, BKC, false, false>), grid,
                            dim3(CF::THREADS), 0, s, p);
-    else if (ragged)
-        hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC, true, true>), grid,
-                           dim3(CF::THREADS), 0, s, p);
-    else
-        hipLaunchKernelGGL((gemm_mfma_kernel<CF, BF, AKC, BKC, true, false>), grid,
-                           dim3(CF::THREADS), 0, s, p);
+    else if constexpr (can_vec) {
+        if (ragged)
+            hipLaunchKernelGGL((gemm_mfma_kernel<CF, IT, AKC, BKC, true, true>), grid,
+                               dim3(CF::THREADS), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_mfma_kernel<CF, IT, AKC, BKC, true, false>), grid,
+                               dim3(CF::THREADS), 0, s, p);
+    }
     return hipGetLastError();
 }
 
-template <class CF, bool BF>
+template <class CF, int IT>
 hipError_t launch_layouts(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
     if (akc)
-        return bkc ? launch_one<CF, BF, true, true>(p, grid, s)
-                   : launch_one<CF, BF, true, false>(p, grid, s);
-    return bkc ? launch_one<CF, BF, false, true>(p, grid, s)
-               : launch_one<CF, BF, false, false>(p, grid, s);
+        return bkc ? launch_one<CF, IT, true, true>(p, grid, s)
+                   : launch_one<CF, IT, true, false>(p, grid, s);
+    return bkc ? launch_one<CF, IT, false, true>(p, grid, s)
+               : launch_one<CF, IT, false, false>(p, grid, s);
 }
 
 }  // namespace libgemm

@@ -47,8 +47,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
-enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+// dtype codes of the C ABI (C, D and out_dtype)
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
+// input (A, B) element types of the kernels
+enum { IT_F16 = 0, IT_BF16 = 1, IT_I8 = 2 };
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Keeps
 // every accumulator index a constant so the accumulators stay in registers.
@@ -95,27 +100,34 @@ struct Params {
 
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 
-// Block-tile configuration.  MF = 32 selects the 32x32x16 MFMA, 16 the
-// 16x16x32 one.  Waves form a WAVES_M x WAVES_N grid over the block tile.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MF_, int GROUP_M_>
+// Block-tile configuration.  MF = 32 selects the 32x32 MFMA (32x32x16 for
+// 16-bit inputs, 32x32x32 for int8), 16 the 16x16 one (16x16x32, 16x16x64).
+// Waves form a WAVES_M x WAVES_N grid over the block tile.  ES is the input
+// element size in bytes; BK counts elements, so an LDS row holds BK*ES bytes.
+// Both MFMA shapes take 16 bytes of each operand per lane, so in bytes the
+// int8 and the 16-bit tiles have the same layout.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MF_, int GROUP_M_,
+          int ES_ = 2>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int MF = MF_;
-    static constexpr int KSTEP = (MF == 32) ? 16 : 32;  // k consumed by one MFMA
+    static constexpr int ES = ES_;
+    static constexpr int KSTEP = ((MF == 32) ? 32 : 64) / ES;  // k consumed by one MFMA
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int TM = WTM / MF, TN = WTN / MF;
-    static constexpr int CH = BK / 8;  // 16-byte chunks per LDS row
+    static constexpr int CH = BK * ES / 16;  // 16-byte chunks per LDS row
     static constexpr int GROUP_M = GROUP_M_;
     static_assert(MF == 32 || MF == 16, "MFMA shape");
-    static_assert(BK % 64 == 0, "the LDS swizzle assumes rows of >= 128 bytes");
+    static_assert(ES == 1 || ES == 2, "element size");
+    static_assert((BK * ES) % 128 == 0, "the LDS swizzle assumes rows of >= 128 bytes");
     static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "row groups of 8");
 };
 
 // ---------------------------------------------------------------- LDS layout
-// Row r of an operand tile holds BK k-values (CH chunks of 8).  Chunk c is
+// Row r of an operand tile holds BK k-values (CH 16-byte chunks).  Chunk c is
 // stored at position c ^ swz(r).  Eight consecutive rows read at one chunk,
 // and eight rows 8 apart written at one chunk, land in eight different
 // 16-byte bank groups.
@@ -168,15 +180,27 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
     return v;
 }
 
+// Keep the first n (0..16) bytes of a 16-byte chunk, zero the rest.
+__device__ __forceinline__ u32x4 keep_first_bytes(u32x4 v, int n) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int b = n - 4 * q;  // bytes of dword q to keep
+        const uint32_t m = b >= 4 ? 0xffffffffu : (b <= 0 ? 0u : ((1u << (8 * b)) - 1u));
+        v[q] &= m;
+    }
+    return v;
+}
+
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
                                             uint32_t soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff,
                                                                             (int)soff, 0));
 }
 
-template <int ROWS, int BK, int THREADS>
+template <int ROWS, int BK, int THREADS, int ES = 2>
 struct LoaderKC {
-    static constexpr int CH = BK / 8;
+    static constexpr int CH = BK * ES / 16;
+    static constexpr int EPC = 16 / ES;  // elements per 16-byte chunk
     static constexpr int TOTAL = ROWS * CH;  // 16-byte chunks in the tile
     static constexpr bool PARTIAL = TOTAL < THREADS;
     static constexpr int PER = PARTIAL ? 1 : TOTAL / THREADS;
@@ -192,23 +216,24 @@ struct LoaderKC {
     }
 
     __device__ __forceinline__ void init(int tid, int64_t ld, int r0, int R) {
-        kc = (chunk(0, tid) % CH) * 8;
+        kc = (chunk(0, tid) % CH) * EPC;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int r = min(r0 + chunk(i, tid) / CH, R - 1);
-            voff[i] = (uint32_t)(((int64_t)r * ld + kc) * 2);
+            voff[i] = (uint32_t)(((int64_t)r * ld + kc) * ES);
         }
     }
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) v[i] = buf_load16(rsrc, voff[i], (uint32_t)k0 * 2u);
+        for (int i = 0; i < PER; ++i)
+            v[i] = buf_load16(rsrc, voff[i], (uint32_t)k0 * (uint32_t)ES);
     }
 
     // the idx-th global load / LDS store of load() / store(), one instruction
     template <int idx>
     __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t) {
-        v[idx] = buf_load16(rsrc, voff[idx], (uint32_t)k0 * 2u);
+        v[idx] = buf_load16(rsrc, voff[idx], (uint32_t)k0 * (uint32_t)ES);
     }
     template <int idx>
     __device__ __forceinline__ void store_one(u32x4 *lds, int tid) const {
@@ -218,24 +243,38 @@ struct LoaderKC {
     }
 
     __device__ __forceinline__ void mask(int k0, int kend) {
-        const int n = min(max(kend - (k0 + kc), 0), 8);
+        const int n = min(max(kend - (k0 + kc), 0), EPC);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) v[i] = keep_first(v[i], n);
+        for (int i = 0; i < PER; ++i) v[i] = ES == 2 ? keep_first(v[i], n) : keep_first_bytes(v[i], n);
     }
 
+    // Element-wise loads with zero fill.  RCADDR: the operand is stored
+    // R-contiguous (X(r,k) = X[k*ld + r]); the chunks are still K-contiguous.
+    template <bool RCADDR>
     __device__ __forceinline__ void load_checked(const uint16_t *X, int64_t ld, int r0, int k0,
                                                  int R, int Kend, int tid) {
+        const uint8_t *X8 = reinterpret_cast<const uint8_t *>(X);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int q = chunk(i, tid);
             const int r = q / CH, c = q % CH;
-            const int gr = r0 + r, gk = k0 + c * 8;
-            uint32_t h[8];
+            const int gr = r0 + r, gk = k0 + c * EPC;
+            uint32_t h[EPC];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                h[e] = (gr < R && gk + e < Kend) ? (uint32_t)X[(int64_t)gr * ld + gk + e] : 0u;
-            v[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                         h[6] | (h[7] << 16)};
+            for (int e = 0; e < EPC; ++e) {
+                const int64_t off = RCADDR ? (int64_t)(gk + e) * ld + gr : (int64_t)gr * ld + gk + e;
+                const bool in = gr < R && gk + e < Kend;
+                h[e] = in ? (ES == 2 ? (uint32_t)X[off] : (uint32_t)X8[off]) : 0u;
+            }
+            if constexpr (ES == 2) {
+                v[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                             h[6] | (h[7] << 16)};
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    v[i][d] = h[4 * d] | (h[4 * d + 1] << 8) | (h[4 * d + 2] << 16) |
+                              (h[4 * d + 3] << 24);
+            }
         }
     }
 
@@ -306,6 +345,7 @@ struct LoaderRC {
                 if (k0 + kg[j] * KB + kk >= kend) v[j][kk] = u32x4{0u, 0u, 0u, 0u};
     }
 
+    template <bool RCADDR>  // always R-contiguous here
     __device__ __forceinline__ void load_checked(const uint16_t *X, int64_t ld, int r0, int k0,
                                                  int R, int Kend, int tid) {
 #pragma unroll
@@ -393,24 +433,36 @@ struct LoaderRC {
 };
 
 // ------------------------------------------------------------------- MFMA
-template <bool BF>
+// int8: the accumulators hold int32 bit patterns in the same float vectors
+// (only moved, never used as floats until the epilogue reinterprets them).
+template <int IT>
 __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
-    if constexpr (BF)
+    if constexpr (IT == IT_BF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    else
+    else if constexpr (IT == IT_F16)
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_bit_cast(
+            f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                           __builtin_bit_cast(i32x4, b),
+                                                           __builtin_bit_cast(i32x16, c), 0, 0, 0));
 }
 
-template <bool BF>
+template <int IT>
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
-    if constexpr (BF)
+    if constexpr (IT == IT_BF16)
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    else
+    else if constexpr (IT == IT_F16)
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                          __builtin_bit_cast(i32x4, b),
+                                                          __builtin_bit_cast(i32x4, c), 0, 0, 0));
 }
 
 template <int MF> struct AccT;
@@ -522,6 +574,12 @@ __device__ __forceinline__ void finish_store(const Params &p, int64_t i, int64_t
     else finish_store_t<DT_BF16>(p, i, j, v);
 }
 
+// int64 -> int32: modulo 2^32, or with satf clamped to the int32 range.
+__device__ __forceinline__ int32_t to_int32(int64_t t, int satf) {
+    if (satf) return (int32_t)(t > INT32_MAX ? INT32_MAX : (t < INT32_MIN ? INT32_MIN : t));
+    return (int32_t)(uint32_t)(uint64_t)t;
+}
+
 // satf on a rounded fp32 value: +-Inf -> +-MAX_NORM, NaN -> +0.
 __device__ __forceinline__ float satf_f32(float x) {
     if (__builtin_isnan(x)) return 0.0f;
@@ -565,6 +623,31 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
             for (int e = 0; e < nval; ++e) w[e] = v[e];
         }
         return;
+    } else if constexpr (OUT == DT_I32) {
+        // int32: the accumulators hold the exact sum (or its value modulo
+        // 2^32 beyond 2^17 products); + C in 64 bits, then wrap or clamp
+        const i32x4 sv = __builtin_bit_cast(i32x4, v);
+        int64_t t[4] = {sv[0], sv[1], sv[2], sv[3]};
+        if (p.C) {
+            const int32_t *cp = reinterpret_cast<const int32_t *>(p.C);
+            if (FULL) {
+                const i32x4 c = *reinterpret_cast<const i32x4 *>(cp + (int64_t)i * p.ldc + j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] += c[e];
+            } else {
+                for (int e = 0; e < nval; ++e)
+                    t[e] += cp[p.c_col ? (int64_t)(j + e) * p.ldc + i : (int64_t)i * p.ldc + j + e];
+            }
+        }
+        i32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = to_int32(t[e], p.satf);
+        int32_t *d = reinterpret_cast<int32_t *>(p.D) + (int64_t)i * p.ldd + j;
+        if (FULL) {
+            *reinterpret_cast<i32x4 *>(d) = o;
+        } else {
+            for (int e = 0; e < nval; ++e) d[e] = o[e];
+        }
     } else {
         // C(i, j..j+3): one vector load when FULL (then C is row-major)
         auto c4 = [&]() {
@@ -671,19 +754,22 @@ __device__ __forceinline__ void map_tile(const Params &p, int w, int &tm, int &t
 // two tiles later and the stores of tile t+1 before its reads.  The body has
 // no branches: past the last K-tile the loads re-read it and the stores and
 // reads go to the idle stage.
-template <class CF, bool BF, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
+template <class CF, int IT, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
 __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg, int kend,
                                        typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
                                        u32x4 *sA, u32x4 *sB, int tid) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, CH = CF::CH;
     constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN, THREADS = CF::THREADS;
     constexpr int KS = BK / CF::KSTEP;           // MFMA steps per K-tile
-    constexpr int KCH = CF::KSTEP / 8;            // LDS chunks per MFMA step
+    constexpr int KCH = CF::KSTEP * CF::ES / 16;  // 16-byte LDS chunks per MFMA step
     static_assert(KS % 2 == 0 && KS >= 4, "fragment slots alternate across K-tiles; the"
                   " store, load and barrier steps are distinct");
-    using LA = typename std::conditional<A_KC, LoaderKC<BM, BK, THREADS>,
+    // 8-bit operands always use K-contiguous chunks: the vector path needs
+    // K-contiguous storage, the element-wise path gathers by layout
+    static_assert(CF::ES == 2 || !VEC || (A_KC && B_KC), "int8 vector loads need K-contiguous A, B");
+    using LA = typename std::conditional<A_KC || CF::ES == 1, LoaderKC<BM, BK, THREADS, CF::ES>,
                                          LoaderRC<BM, BK, THREADS>>::type;
-    using LB = typename std::conditional<B_KC, LoaderKC<BN, BK, THREADS>,
+    using LB = typename std::conditional<B_KC || CF::ES == 1, LoaderKC<BN, BK, THREADS, CF::ES>,
                                          LoaderRC<BN, BK, THREADS>>::type;
 
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
@@ -707,8 +793,8 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
                 lb.mask(k0, kend);
             }
         } else {
-            la.load_checked(p.A, p.lda, m0, k0, p.M, kend, tid);
-            lb.load_checked(p.B, p.ldb, n0, k0, p.N, kend, tid);
+            la.template load_checked<!A_KC>(p.A, p.lda, m0, k0, p.M, kend, tid);
+            lb.template load_checked<!B_KC>(p.B, p.ldb, n0, k0, p.N, kend, tid);
         }
     };
 
@@ -749,9 +835,9 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
         // the transposed tile, whose rows (D columns) land in consecutive
         // accumulator registers of one lane (see acc_col)
         if constexpr (MF == 32)
-            acc[i][j] = mfma32<BF>(fb[sl][j], fa[sl][i], acc[i][j]);
+            acc[i][j] = mfma32<IT>(fb[sl][j], fa[sl][i], acc[i][j]);
         else
-            acc[i][j] = mfma16<BF>(fb[sl][j], fa[sl][i], acc[i][j]);
+            acc[i][j] = mfma16<IT>(fb[sl][j], fa[sl][i], acc[i][j]);
     };
     auto store_one = [&](int buf, auto w_tag) {
         constexpr int w = decltype(w_tag)::value;
@@ -871,7 +957,7 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
 // VEC selects the vector (aligned) or the element-wise (unaligned) loads and
 // RAGGED whether the vector loads mask k >= kend; each combination is its own
 // kernel, with a single K loop to allocate registers for.
-template <class CF, bool BF, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
+template <class CF, int IT, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
 __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     constexpr int BM = CF::BM, BN = CF::BN, CH = CF::CH;
     constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
@@ -899,7 +985,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         });
     });
 
-    k_loop<CF, BF, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
+    k_loop<CF, IT, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
 
     // Epilogue.  Each lane owns 4 consecutive columns of one row per register
     // group.  Interior tiles with vector-friendly C/D and the plain epilogue
@@ -929,7 +1015,8 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         });
     };
     if (full && !p.epi) {
-        if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
+        if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{});
+        else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
         else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
         else direct(std::integral_constant<int, DT_BF16>{});
         return;
@@ -970,6 +1057,9 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                 const int gi = row0 + i * MF + rr, gj = col0 + c4;
                 if (p.splits > 1) {
                     finish4<-1, false, false>(p, gi, gj, v);
+                } else if constexpr (IT == IT_I8) {  // int32 out, plain epilogue only
+                    if (full) finish4<DT_I32, true, false>(p, gi, gj, v);
+                    else finish4<DT_I32, false, false>(p, gi, gj, v);
                 } else if (full) {  // interior tile, extended epilogue
                     if (p.out_dtype == DT_F32) finish4<DT_F32, true, true>(p, gi, gj, v);
                     else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true>(p, gi, gj, v);

@@ -5,6 +5,6 @@
 
 namespace libgemm {
 hipError_t launch_large8_bf16(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
-    return launch_layouts<CfgLarge8, true>(p, akc, bkc, grid, s);
+    return launch_layouts<CfgLarge8, IT_BF16>(p, akc, bkc, grid, s);
 }
 }  // namespace libgemm

@@ -5,6 +5,6 @@
 
 namespace libgemm {
 hipError_t launch_large_f16(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
-    return launch_layouts<CfgLarge, false>(p, akc, bkc, grid, s);
+    return launch_layouts<CfgLarge, IT_F16>(p, akc, bkc, grid, s);
 }
 }  // namespace libgemm

@@ -5,6 +5,6 @@
 
 namespace libgemm {
 hipError_t launch_medium_f16(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
-    return launch_layouts<CfgMedium, false>(p, akc, bkc, grid, s);
+    return launch_layouts<CfgMedium, IT_F16>(p, akc, bkc, grid, s);
 }
 }  // namespace libgemm

@@ -5,6 +5,6 @@
 
 namespace libgemm {
 hipError_t launch_skinny_f16(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
-    return launch_layouts<CfgSkinny, false>(p, akc, bkc, grid, s);
+    return launch_layouts<CfgSkinny, IT_F16>(p, akc, bkc, grid, s);
 }
 }  // namespace libgemm

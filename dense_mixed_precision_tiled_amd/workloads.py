@@ -308,3 +308,57 @@ def make_epilogue_problem(M: int, N: int, K: int, *, layoutA=ROW_MAJOR, layoutB=
     return EpilogueProblem(name, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC,
                            D, ldd, layoutD, in_dtype, acc_dtype, out_dtype, satf,
                            float(alpha), float(beta), bias, int(act), inplace)
+
+
+# ------------------------------------------------ int8 x int8 -> int32 problems
+
+I8, I32 = 3, 4
+PAD_I8 = np.int8(-128)          # A/B padding: changes any sum that reads it
+SENTINEL_I32 = np.int32(0x5A5A5A5A)
+
+
+def _int8_operand(rng, rows: int, cols: int, ld: int, values: str) -> np.ndarray:
+    buf = np.full((rows, ld), PAD_I8, dtype=np.int8)
+    if rows and cols:
+        lo, hi = (-128, 128) if values == "full" else (-3, 4)
+        buf[:, :cols] = rng.integers(lo, hi, size=(rows, cols)).astype(np.int8)
+    return buf
+
+
+def make_int8_problem(M: int, N: int, K: int, *, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+                      values="full", c_values: Optional[str] = None, inplace=False, satf=0,
+                      lda=None, ldb=None, ldc=None, ldd=None, seed=7777,
+                      name="int8") -> Problem:
+    """Seeded int8 A, B (``full``: uniform over [-128, 127]; ``small``: [-3, 3])
+    and int32 C (``int``: [-1000, 1000]; ``big``: the whole int32 range), all
+    row-major C/D.  A/B padding holds -128, D a sentinel."""
+    rng_a = np.random.default_rng(seed)
+    rng_b = np.random.default_rng(seed + 1)
+    rng_c = np.random.default_rng(seed + 2)
+    a_outer, a_inner = (M, K) if layoutA == ROW_MAJOR else (K, M)
+    b_outer, b_inner = (K, N) if layoutB == ROW_MAJOR else (N, K)
+    lda = max(1, a_inner) if lda is None else lda
+    ldb = max(1, b_inner) if ldb is None else ldb
+    ldd = max(1, N) if ldd is None else ldd
+    A = _int8_operand(rng_a, a_outer, a_inner, lda, values)
+    B = _int8_operand(rng_b, b_outer, b_inner, ldb, values)
+    D = np.full((M, ldd), SENTINEL_I32, dtype=np.int32)
+
+    def draw_c(shape):
+        if c_values == "big":
+            return rng_c.integers(-2 ** 31, 2 ** 31, size=shape, dtype=np.int64).astype(np.int32)
+        return rng_c.integers(-1000, 1001, size=shape).astype(np.int32)
+
+    C = None
+    if inplace:
+        ldc = ldd
+        D[:, :N] = draw_c((M, N))
+        C = D
+    elif c_values is not None:
+        ldc = max(1, N) if ldc is None else ldc
+        C = np.full((M, ldc), SENTINEL_I32, dtype=np.int32)
+        C[:, :N] = draw_c((M, N))
+    else:
+        ldc = max(1, N) if ldc is None else ldc
+    return Problem(name, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                   I8, I32, I32, satf, inplace)

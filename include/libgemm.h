@@ -18,6 +18,9 @@
  *    section "WMMA API解释" item (5) mma_sync.
  *  - fp16-accumulate HGEMM variant (fp16 A, B, C, D):
  *    "hgemm_mma_m16n8k16_naive_kernel", section 1.1 "m16n8k16 指令规格".
+ *  - int8 inputs with an int32 accumulator: the fragment type lists of
+ *    "CUDA算子优化(5)：WMMA矩阵乘法" (char operands, int accumulator) and
+ *    "深入CUDA Tensor Core与WMMA…", section 2.3 (INT8 on the matrix units).
  *
  * Readings where the pages leave a step open:
  *  - C and D are row-major (C(i,j) = C[i*ldc + j]); C has the output dtype.
@@ -30,6 +33,9 @@
  *  - Rounding to fp16 / bf16 is round-to-nearest-even.
  *  - Nothing outside rows [0,M) and columns [0,N) of D is written, and no
  *    element of A or B outside the M x K and K x N matrices is read.
+ *  - int8 (in_dtype GEMM_I8, acc and out GEMM_I32): the sum is exact; the
+ *    result (+ C) wraps modulo 2^32, or with satf is clamped to the int32
+ *    range.  satf needs K < 2^17, where the int32 accumulator cannot wrap.
  */
 #ifndef LIBGEMM_H
 #define LIBGEMM_H
@@ -50,7 +56,9 @@ typedef enum {
 typedef enum {
     GEMM_F32 = 0,  /* IEEE binary32 */
     GEMM_F16 = 1,  /* IEEE binary16 */
-    GEMM_BF16 = 2  /* bfloat16 (upper half of binary32) */
+    GEMM_BF16 = 2, /* bfloat16 (upper half of binary32) */
+    GEMM_I8 = 3,   /* two's-complement 8-bit integer (A, B)  */
+    GEMM_I32 = 4   /* two's-complement 32-bit integer (C, D, accumulator) */
 } gemm_dtype_t;
 
 /* Return codes.  GEMM_OK means "validated and enqueued". */
@@ -81,11 +89,14 @@ typedef enum {
  *                may be NULL (C = 0).  C == D with ldc == ldd is the in-place
  *                update C = A x B + C; any other overlap of C and D is rejected.
  *   D, ldd       device pointer to out_dtype elements, row-major, ldd >= N.
- *   in_dtype     GEMM_F16 or GEMM_BF16.
+ *   in_dtype     GEMM_F16, GEMM_BF16, or GEMM_I8 (A and B int8).
  *   acc_dtype    GEMM_F32 (out_dtype F32, F16 or BF16), or GEMM_F16 with
- *                in_dtype == out_dtype == GEMM_F16 (HGEMM).
+ *                in_dtype == out_dtype == GEMM_F16 (HGEMM), or GEMM_I32 with
+ *                in_dtype GEMM_I8 and out_dtype GEMM_I32.
  *   out_dtype    dtype of C and D.
- *   satf         nonzero: +Inf -> +MAX_NORM, -Inf -> -MAX_NORM, NaN -> +0.
+ *   satf         nonzero: +Inf -> +MAX_NORM, -Inf -> -MAX_NORM, NaN -> +0;
+ *                for int32 output: clamp to [-2^31, 2^31-1] instead of wrapping
+ *                (int8 with K >= 2^17 and satf: GEMM_ERR_UNSUPPORTED).
  *   stream       a hipStream_t (NULL = the null stream).  The work is enqueued
  *                on it; the call does not wait for it.
  *
@@ -101,8 +112,9 @@ typedef enum {
  * synchronisation of the stream.
  *
  * Speed: 16-byte vector loads are used where A and B base pointers are
- * 16-byte aligned and lda, ldb are multiples of 8 elements (the pages' ldm
- * rule); any other alignment runs correct element-wise loads.
+ * 16-byte aligned and lda, ldb are multiples of 16 bytes (the pages' ldm
+ * rule), for int8 only with A row-major and B column-major (both
+ * K-contiguous); anything else runs correct element-wise loads.
  */
 int gemm_run(int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda, int layoutA,
@@ -148,7 +160,8 @@ int gemm_run_config(int config_id,
 
 /*
  * Host-only argument check of gemm_run (no HIP call, no device needed):
- * returns GEMM_OK or the error gemm_run would return before enqueuing.
+ * returns GEMM_OK or the error gemm_run would return before enqueuing, except
+ * the int8 satf limit on K, which depends on satf.
  */
 int gemm_validate(int64_t M, int64_t N, int64_t K,
                   const void *A, int64_t lda, int layoutA,
@@ -203,8 +216,9 @@ typedef struct {
  *   ldc, ldd     >= N for a row-major matrix, >= M for a column-major one.
  *   C == D       (in place) needs ldc == ldd and layoutC == layoutD.
  *   bias         N fp32 values on the device; must not overlap D.
- * Errors, in addition to gemm_run's: an activation outside gemm_activation_t
- * -> GEMM_ERR_UNSUPPORTED; layoutC / layoutD not a gemm_layout_t ->
+ * Errors, in addition to gemm_run's: an activation outside gemm_activation_t,
+ * or int8 inputs with anything but the plain epilogue (alpha = 1, beta 1 or
+ * 0, no bias, no activation; C/D layouts are fine) -> GEMM_ERR_UNSUPPORTED; layoutC / layoutD not a gemm_layout_t ->
  * GEMM_ERR_INVALID_LAYOUT; bias overlapping D, or C == D with different
  * layouts or leading dimensions -> GEMM_ERR_ALIASING.
  *

@@ -61,6 +61,11 @@ def test_dispatcher_shape_classes(lib):
     assert pick(16384, 16384, 1024).startswith("large")
     assert pick(16, 16384, 16384).startswith("skinny")
     assert pick(256, 256, 256).startswith("small")
+    I8, I32 = lg.GEMM_I8, lg.GEMM_I32
+    pick8 = lambda M, N, K: names[lg.gemm_select_config(M, N, K, R, Cm, I8, I32, I32)]
+    assert pick8(4096, 4096, 4096).startswith("i8_large8")
+    assert pick8(16, 16384, 16384).startswith("i8_skinny")
+    assert pick8(256, 256, 256).startswith("i8_small")
     assert lg.gemm_select_config(-1, 4, 4, R, R, F16, F32, F32) == -1
     assert lg.gemm_select_config(4, 4, 4, 7, R, F16, F32, F32) == -5
     assert lg.gemm_select_config(4, 4, 4, R, R, F32, F32, F32) == -4
@@ -90,6 +95,9 @@ def test_validation_ok_cases(lib):
     assert v(N=0, A=None, B=None, D=None) == 0
     assert v(K=0, A=None, B=None, lda=1, ldb=8) == 0   # K = 0: A, B unused
     assert v(lda=13, ldb=9, ldd=11) == 0     # padded (unaligned) leading dims
+    I8, I32 = lg.GEMM_I8, lg.GEMM_I32
+    assert v(i=I8, a=I32, o=I32) == 0        # int8 x int8 -> int32
+    assert v(i=I8, a=I32, o=I32, C=C0, la=Cm, lb=R) == 0
 
 
 def test_validation_errors(lib):
@@ -103,6 +111,9 @@ def test_validation_errors(lib):
     assert v(i=F32) == -4 and v(a=BF16) == -4
     assert v(i=BF16, a=F16, o=F16) == -4 and v(a=F16, o=F32) == -4
     assert v(la=2) == -5 and v(lb=-1) == -5
+    I8, I32 = lg.GEMM_I8, lg.GEMM_I32
+    assert v(i=I8, a=F32, o=F32) == -4 and v(i=I8, a=I32, o=F32) == -4
+    assert v(i=F16, a=I32, o=I32) == -4 and v(i=F16, a=F32, o=I32) == -4
     assert v(D=A0 + 64) == -6                # D inside A
     assert v(D=B0) == -6
     assert v(C=D0 + 4) == -6                 # C partially overlaps D

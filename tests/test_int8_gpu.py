@@ -1,0 +1,158 @@
+"""GPU parity of int8 x int8 -> int32 (in_dtype GEMM_I8) through the C ABI
+against the oracle's gemm_i8.  Integer results are compared bit for bit."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import dense_mixed_precision_tiled_amd as lg
+import oracle
+from dense_mixed_precision_tiled_amd import workloads as W
+from dense_mixed_precision_tiled_amd.workloads import COL_MAJOR, F16, F32, ROW_MAJOR
+from gpu_util import DeviceProblem, log
+
+pytestmark = pytest.mark.gpu
+
+I8, I32 = lg.GEMM_I8, lg.GEMM_I32
+# int8 tile-table entries -> block tile edge (None: skinny split-K)
+I8_ENTRY_TILE = {5: 256, 6: 128, 7: 64, 8: None}
+
+
+def _shape(cid):
+    bm = I8_ENTRY_TILE[cid]
+    return (13, 3 * 128 - 5, 2200) if bm is None else (2 * bm + 17, 3 * bm - 5, 400)
+
+
+def oracle_i8(prob, layoutD=ROW_MAJOR):
+    D = prob.D.copy()
+    C = D if prob.inplace else prob.C
+    oracle.gemm_i8(prob.M, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                   prob.B.ravel(), prob.ldb, prob.layoutB, None if C is None else C.ravel(),
+                   prob.ldc, ROW_MAJOR, D.ravel(), prob.ldd, layoutD, prob.satf)
+    return D
+
+
+def _check(prob, config=None, label=""):
+    log("case: %s config=%s" % (label, config))
+    dp = DeviceProblem(prob)
+    dp.run(config=config)
+    got = dp.result()
+    ref = oracle_i8(prob)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, "%s: %d of %d differ, e.g. %s got %s ref %s" % (
+        label, len(bad), got.size, bad[:3].tolist(), got[tuple(bad[:3].T)], ref[tuple(bad[:3].T)])
+
+
+def test_int8_entries_are_in_the_table():
+    for cid, bm in I8_ENTRY_TILE.items():
+        name = lg.gemm_config_name(cid)
+        assert name.startswith("i8_"), name
+        if bm is not None:
+            assert "_%dx%dx" % (bm, bm) in name, name
+
+
+@pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, COL_MAJOR), (ROW_MAJOR, ROW_MAJOR),
+                                   (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)])
+def test_every_int8_entry_and_layout(cid, la, lb):
+    M, N, K = _shape(cid)
+    prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="full", c_values="big",
+                               ldd=N + 3, seed=8000 + cid)
+    _check(prob, cid, "i8 cfg%d A%d B%d" % (cid, la, lb))
+
+
+@pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
+def test_satf_clamps_and_in_place(cid):
+    M, N, K = _shape(cid)
+    # C spans the whole int32 range, so C + A x B leaves it for some outputs
+    prob = W.make_int8_problem(M, N, K, values="full", c_values="big", inplace=True, satf=1,
+                               ldd=N + 1, seed=8100 + cid)
+    _check(prob, cid, "i8 cfg%d satf in place" % cid)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (5, 7, 3), (33, 65, 129), (70, 45, 0),
+                                   (64, 64, 4096 + 17)])
+def test_small_and_ragged_shapes(shape):
+    M, N, K = shape
+    prob = W.make_int8_problem(M, N, K, values="full", c_values="int", seed=8200 + M)
+    _check(prob, None, "i8 %dx%dx%d" % shape)
+
+
+def test_unaligned_leading_dims_take_the_element_path():
+    prob = W.make_int8_problem(100, 90, 300, lda=301, ldb=303, ldd=95, values="full",
+                               c_values="int", seed=8300)
+    _check(prob, None, "i8 unaligned")
+
+
+def test_wraps_modulo_2_32_beyond_2_17_products():
+    """K = 140000 products of magnitude up to 2^14: sums leave the int32 range
+    and wrap, exactly as the oracle's modular reduction of the exact sum."""
+    M, N, K = 64, 64, 140000
+    prob = W.make_int8_problem(M, N, K, values="full", c_values=None, seed=8400)
+    # push sums past 2^31: most rows all +127 or -128
+    prob.A[:, :K] = np.where(np.arange(M)[:, None] % 3 == 0, -128, 127).astype(np.int8)
+    prob.B[:, :K] = np.int8(127)
+    ref = oracle_i8(prob)
+    exact = [int(np.int64(K) * int(prob.A[i, 0]) * 127) for i in range(M)]
+    assert any(abs(e) > 2 ** 31 for e in exact)
+    _check(prob, None, "i8 wrap")
+
+
+def test_satf_with_k_at_or_above_2_17_is_rejected():
+    prob = W.make_int8_problem(8, 8, 1 << 17, values="small", satf=1, seed=8500)
+    dp = DeviceProblem(prob)
+    with pytest.raises(lg.GemmError) as e:
+        dp.run()
+    assert e.value.status == -4
+
+
+def test_column_major_d_and_rejected_epilogues():
+    M, N, K = 300, 200, 256
+    prob = W.make_int8_problem(M, N, K, values="full", c_values=None, seed=8600)
+    dp = DeviceProblem(prob)
+    Dc = torch.full((N, M), 7, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    args = (M, N, K, dp.A.data_ptr(), prob.lda, prob.layoutA, dp.B.data_ptr(), prob.ldb,
+            prob.layoutB, None, prob.ldc, Dc.data_ptr(), M, I8, I32, I32, 0)
+    assert lg.gemm_run_ex(*args, lg.GemmEpilogue(layoutD=COL_MAJOR), s) == 0
+    torch.cuda.synchronize()
+    ref = np.zeros(N * M, dtype=np.int32)
+    oracle.gemm_i8(M, N, K, prob.A.ravel(), prob.lda, prob.layoutA, prob.B.ravel(), prob.ldb,
+                   prob.layoutB, None, N, ROW_MAJOR, ref, M, COL_MAJOR, 0)
+    assert np.array_equal(Dc.cpu().numpy().ravel(), ref)
+    for epi in (lg.GemmEpilogue(alpha=2.0), lg.GemmEpilogue(activation=lg.GEMM_ACT_RELU)):
+        assert lg.gemm_run_ex(*args, epi, s) == -4
+
+
+def test_config_class_mismatch_is_rejected():
+    prob = W.make_int8_problem(64, 64, 64, values="small", seed=8700)
+    dp = DeviceProblem(prob)
+    with pytest.raises(lg.GemmError) as e:
+        dp.run(config=0)          # a 16-bit entry
+    assert e.value.status == -8
+    f16 = W.make_problem(64, 64, 64, values="int", seed=8701)
+    with pytest.raises(lg.GemmError) as e:
+        DeviceProblem(f16).run(config=5)   # an int8 entry
+    assert e.value.status == -8
+
+
+def test_4096_int8_sampled():
+    """The int8 workload the benchmark times: 4096^3, A row-major, B
+    column-major, int32 D; 4096 sampled outputs against the sampled oracle,
+    and the row/column sums of D against those of the inputs (exact)."""
+    n = 4096
+    prob = W.make_int8_problem(n, n, n, values="full", c_values=None, seed=8800)
+    log("case: i8 4096^3")
+    dp = DeviceProblem(prob)
+    dp.run()
+    got = dp.result()
+    rows, cols = W.sample_indices(n, n, 4096, seed=8801)
+    ref = oracle.gemm_i8_sampled(n, n, n, prob.A.ravel(), prob.lda, prob.layoutA, prob.B.ravel(),
+                                 prob.ldb, prob.layoutB, None, prob.ldc, ROW_MAJOR, rows, cols, 0)
+    assert np.array_equal(got[rows, cols], ref)
+    # sum_j D(i,j) = sum_k A(i,k) * (sum_j B(k,j)) exactly (|D| < 2^31 here)
+    A64 = prob.A[:, :n].astype(np.int64)
+    Bk = prob.B[:, :n].astype(np.int64)          # column-major: B(k,j) = Bk[j,k]
+    assert np.array_equal(got.astype(np.int64).sum(axis=1), A64 @ Bk.sum(axis=0))
+    assert np.array_equal(got.astype(np.int64).sum(axis=0), Bk @ A64.sum(axis=0))
