@@ -17,6 +17,7 @@ arrays through ctypes.  Definitions followed (page title, section):
   same page sections 3.2 and 4.2;
 * in-place ``C = A*B + C`` and saturate-to-finite:
   "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释" item (5);
+* OCP fp8 inputs (E4M3, E5M2; one byte per element) in every float function;
 * int8 x int8 -> int32 (``gemm_i8``): the type lists of
   "CUDA算子优化(5)：WMMA矩阵乘法" and "深入CUDA Tensor Core与WMMA…" section 2.3;
 * the extended epilogue ``D = act(alpha*(A x B) + beta*C + bias)`` with row- or
@@ -46,6 +47,7 @@ F32, F16, BF16 = 0, 1, 2
 ROW_MAJOR, COL_MAJOR = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 I8, I32 = 3, 4
+FP8_E4M3, FP8_E5M2 = 5, 6
 
 _lib = None
 
@@ -101,6 +103,10 @@ def _load():
                                                vp, i64, c_int, i64, vp, vp, vp, c_int, c_int]
         lib.oracle_activation.restype = dbl
         lib.oracle_activation.argtypes = [dbl, c_int]
+        lib.oracle_decode_fp8_e4m3.restype = ctypes.c_double
+        lib.oracle_decode_fp8_e4m3.argtypes = [ctypes.c_uint8]
+        lib.oracle_decode_fp8_e5m2.restype = ctypes.c_double
+        lib.oracle_decode_fp8_e5m2.argtypes = [ctypes.c_uint8]
         lib.oracle_decode_f16.restype = ctypes.c_double
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_bf16.restype = ctypes.c_double
@@ -127,8 +133,8 @@ def _ptr(a):
 
 
 def _check_in(a):
-    if a.dtype != np.uint16 or not a.flags.c_contiguous:
-        raise TypeError("A/B must be C-contiguous uint16 bit patterns")
+    if a.dtype not in (np.uint16, np.uint8) or not a.flags.c_contiguous:
+        raise TypeError("A/B must be C-contiguous bit patterns (uint16, or uint8 for fp8)")
 
 
 def _check_out(a, out_dtype):
@@ -186,6 +192,14 @@ def element_fp64(K, A, lda, layoutA, B, ldb, layoutB, C, ldc, in_dtype, out_dtyp
     """The fp64 value of sum_k A(i,k)B(k,j) (+ C[i,j]) before the final rounding."""
     return _load().oracle_element_fp64(K, _ptr(A), lda, layoutA, _ptr(B), ldb, layoutB,
                                        _ptr(C), ldc, in_dtype, out_dtype, i, j)
+
+
+def decode_fp8_e4m3(bits: int) -> float:
+    return _load().oracle_decode_fp8_e4m3(bits)
+
+
+def decode_fp8_e5m2(bits: int) -> float:
+    return _load().oracle_decode_fp8_e5m2(bits)
 
 
 def decode_f16(bits: int) -> float:

@@ -28,6 +28,9 @@
  *    -Inf -> -MAX_NORM, NaN -> +0): "CUDA算子优化(5)：WMMA矩阵乘法",
  *    section "WMMA API解释" item (5) mma_sync.
  *
+ * Inputs may also be OCP fp8 (E4M3 or E5M2, one byte per element); see the
+ * decoders below.
+ *
  * Readings where the pages are silent or disagree (each also listed in the
  * design notes):
  *  - acc_dtype F16 ("HGEMM": fp16 accumulator, fp16 C and D) fixes the dtype of
@@ -54,7 +57,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_I8 = 3, ORACLE_I32 = 4,
+       ORACLE_FP8_E4M3 = 5, ORACLE_FP8_E5M2 = 6 };
 enum { ORACLE_ROW_MAJOR = 0, ORACLE_COL_MAJOR = 1 };
 
 /* ---------------------------------------------------------------- decoding */
@@ -82,6 +86,41 @@ double oracle_decode_bf16(uint16_t h)
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/*
+ * OCP 8-bit floating point (the formats the fp8 type lists of the pages refer
+ * to, as defined by the OCP FP8 specification):
+ *   E4M3: 1 sign, 4 exponent bits (bias 7), 3 fraction bits; no infinities,
+ *         S.1111.111 is NaN, the largest finite value is 448;
+ *   E5M2: 1 sign, 5 exponent bits (bias 15), 2 fraction bits; IEEE-style
+ *         infinities (exponent 31, fraction 0) and NaNs.
+ * Exponent field 0 holds subnormals.
+ */
+double oracle_decode_fp8_e4m3(uint8_t b)
+{
+    int sign = (b >> 7) & 1, e = (b >> 3) & 0xf, m = b & 7;
+    double v;
+    if (e == 0xf && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);              /* m * 2^-3 * 2^(1-7) */
+    else
+        v = ldexp((double)(m + 8), e - 10);    /* (8+m) * 2^(e-7-3) */
+    return sign ? -v : v;
+}
+
+double oracle_decode_fp8_e5m2(uint8_t b)
+{
+    int sign = (b >> 7) & 1, e = (b >> 2) & 0x1f, m = b & 3;
+    double v;
+    if (e == 0x1f)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);             /* m * 2^-2 * 2^(1-15) */
+    else
+        v = ldexp((double)(m + 4), e - 17);    /* (4+m) * 2^(e-15-2) */
+    return sign ? -v : v;
 }
 
 /* ---------------------------------------------------------------- encoding */
@@ -201,6 +240,10 @@ static uint32_t finish_element(double s, int out_dtype, int satf)
 
 static double load_in(const void *base, int dtype, int64_t off)
 {
+    if (dtype == ORACLE_FP8_E4M3)
+        return oracle_decode_fp8_e4m3(((const uint8_t *)base)[off]);
+    if (dtype == ORACLE_FP8_E5M2)
+        return oracle_decode_fp8_e5m2(((const uint8_t *)base)[off]);
     uint16_t h = ((const uint16_t *)base)[off];
     return dtype == ORACLE_BF16 ? oracle_decode_bf16(h) : oracle_decode_f16(h);
 }
