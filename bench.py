@@ -99,8 +99,12 @@ WORKLOADS = {
     # int8 x int8 -> int32
     "4096_i8": (None, "M=N=K=4096 GEMM, int8 A row-major and B column-major (uniform over "
                 "[-128,127]), int32 accumulate and D, C=0", "mfma_i8"),
+    # OCP fp8 E4M3 inputs, fp32 accumulate
+    "4096_fp8": (None, "M=N=K=4096 GEMM, fp8 E4M3 A row-major and B column-major "
+                 "(uniform[-1,1] rounded to E4M3), fp32 accumulate and D, C=0", "mfma_fp8"),
 }
 PEAK_I8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
@@ -109,6 +113,9 @@ def make_workload(W, name):
     if name == "4096_f16_bias_gelu":
         prob = W.make_epilogue_problem(4096, 4096, 4096, values="uniform", c_values=None,
                                        bias_values="normal", act=2, ldd=4096, seed=20330)
+    elif name == "4096_fp8":
+        prob = W.make_problem(4096, 4096, 4096, layoutA=0, layoutB=1, in_dtype=W.FP8_E4M3,
+                              values="uniform", seed=20360)
     elif name == "4096_i8":
         prob = W.make_int8_problem(4096, 4096, 4096, values="full", c_values=None, seed=20350)
     elif name == "4096_f16_colD":
@@ -242,7 +249,10 @@ def main():
     achieved = flop / (mean_ms * 1e-3) / 1e12
     traffic = load_traffic() if args.workload == "4096_f16" else None
     nbytes = algorithmic_bytes(prob)
-    if bound == "mfma_i8":
+    if bound == "mfma_fp8":
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4)}
+    elif bound == "mfma_i8":
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_I8_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / PEAK_I8_TOPS, 4)}
     elif bound == "hbm":
@@ -259,7 +269,8 @@ def main():
                                            args.workload),
         "value": round(value, 2),
         "unit": "TOP/s" if prob.in_dtype == 3 else "TFLOP/s",
-        "pct_of_peak": round(100.0 * value / (PEAK_I8_TOPS if prob.in_dtype == 3
+        "pct_of_peak": round(100.0 * value / (PEAK_I8_TOPS if prob.in_dtype == 3 else
+                                               PEAK_FP8_TFLOPS if prob.in_dtype in (5, 6)
                                                else PEAK_TFLOPS), 2),
         "n_gpus": 1,
         "steps": args.steps,
@@ -268,7 +279,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {2: "bf16", 3: "i8"}.get(prob.in_dtype, "f16"),
+        "dtype": {2: "bf16", 3: "i8", 5: "fp8_e4m3", 6: "fp8_e5m2"}.get(prob.in_dtype, "f16"),
         "data": "synthetic",
         "config": {
             "workload": desc,

@@ -21,7 +21,7 @@ import torch  # noqa: F401
 
 __all__ = [
     "GEMM_ROW_MAJOR", "GEMM_COL_MAJOR", "GEMM_F32", "GEMM_F16", "GEMM_BF16", "GEMM_I8",
-    "GEMM_I32",
+    "GEMM_I32", "GEMM_FP8_E4M3", "GEMM_FP8_E5M2",
     "GEMM_OK", "GemmError", "LIB_PATH", "library",
     "gemm_run", "gemm_run_config", "gemm_validate", "gemm_status_string",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config",
@@ -32,6 +32,7 @@ __all__ = [
 
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
 GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_I8, GEMM_I32 = 0, 1, 2, 3, 4
+GEMM_FP8_E4M3, GEMM_FP8_E5M2 = 5, 6
 GEMM_OK = 0
 GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_ACT_GELU = 0, 1, 2
 STATUS_NAMES = {

@@ -45,7 +45,7 @@ struct Entry {
     const char *name;
     int BM, BN, BK;
     int split_k;  // 1: this entry may split K across workgroups
-    int klass;    // input class: 0 = fp16/bf16, 1 = int8
+    int klass;    // input class: 0 = fp16/bf16, 1 = int8, 2 = OCP fp8
     launch_fn launch;
 };
 
@@ -68,13 +68,23 @@ const Entry kTable[] = {
      launch_small_i8},
     {"i8_skinny_16x128x256_w1x4_mfma16x16x64_splitk", CfgSkinnyI8::BM, CfgSkinnyI8::BN,
      CfgSkinnyI8::BK, 1, 1, launch_skinny_i8},
+    {"fp8_large8_256x256x128_w2x4_mfma32x32x64", CfgLarge8F8::BM, CfgLarge8F8::BN,
+     CfgLarge8F8::BK, 0, 2, launch_large8_fp8},
+    {"fp8_medium_128x128x128_w2x2_mfma32x32x64", CfgMediumF8::BM, CfgMediumF8::BN,
+     CfgMediumF8::BK, 0, 2, launch_medium_fp8},
+    {"fp8_small_64x64x128_w2x2_mfma32x32x64", CfgSmallF8::BM, CfgSmallF8::BN, CfgSmallF8::BK, 0,
+     2, launch_small_fp8},
+    {"fp8_skinny_16x128x256_w1x4_mfma16x16x128_splitk", CfgSkinnyF8::BM, CfgSkinnyF8::BN,
+     CfgSkinnyF8::BK, 1, 2, launch_skinny_fp8},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
 enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
-       CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8 };
+       CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8,
+       CFG_F8_LARGE8 = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12 };
 
-int input_class(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : 0; }
-int in_size(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : 2; }
+bool is_fp8(int in_dtype) { return in_dtype == GEMM_FP8_E4M3 || in_dtype == GEMM_FP8_E5M2; }
+int input_class(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : (is_fp8(in_dtype) ? 2 : 0); }
+int in_size(int in_dtype) { return (in_dtype == GEMM_I8 || is_fp8(in_dtype)) ? 1 : 2; }
 
 constexpr int kCUs = 256;  // MI355X compute units
 
@@ -123,7 +133,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
     if (!layout_ok(layoutA) || !layout_ok(layoutB) || !layout_ok(epi->layoutC) ||
         !layout_ok(epi->layoutD))
         return GEMM_ERR_INVALID_LAYOUT;
-    if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16 && in_dtype != GEMM_I8)
+    if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16 && in_dtype != GEMM_I8 && !is_fp8(in_dtype))
         return GEMM_ERR_UNSUPPORTED;
     if (in_dtype == GEMM_I8) {
         // int8 x int8 -> int32: the plain epilogue only (C/D layouts allowed);
@@ -182,13 +192,18 @@ int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
 
 int select_config(int64_t M, int64_t N, int64_t K, int klass) {
     (void)K;
-    const bool i8 = klass == 1;
-    if (M <= CfgSkinny::BM) return i8 ? CFG_I8_SKINNY : CFG_SKINNY;
+    // the same shape classes for every input class; entries per class
+    static const int kByClass[3][4] = {
+        {CFG_SKINNY, CFG_LARGE8, CFG_MEDIUM, CFG_SMALL},
+        {CFG_I8_SKINNY, CFG_I8_LARGE8, CFG_I8_MEDIUM, CFG_I8_SMALL},
+        {CFG_F8_SKINNY, CFG_F8_LARGE8, CFG_F8_MEDIUM, CFG_F8_SMALL}};
+    const int *e = kByClass[klass];
+    if (M <= CfgSkinny::BM) return e[0];
     const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
-    if (t_large >= 3 * kCUs / 4) return i8 ? CFG_I8_LARGE8 : CFG_LARGE8;
+    if (t_large >= 3 * kCUs / 4) return e[1];
     const int64_t t_medium = cdiv(M, CfgMedium::BM) * cdiv(N, CfgMedium::BN);
-    if (t_medium >= kCUs / 2) return i8 ? CFG_I8_MEDIUM : CFG_MEDIUM;
-    return i8 ? CFG_I8_SMALL : CFG_SMALL;
+    if (t_medium >= kCUs / 2) return e[2];
+    return e[3];
 }
 
 // Autotuned choices: problem signature (as the kernels see it, after a
@@ -330,6 +345,7 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
                ((lda * isz) % 16 == 0) && ((ldb * isz) % 16 == 0) &&
                a_rng < ((int64_t)1 << 32) - 16 && b_rng < ((int64_t)1 << 32) - 16 &&
                (isz == 2 || (layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR));
+    // (the 8-bit vector loads need K-contiguous A and B: A row-major, B col-major)
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
     const int osz = out_size(out_dtype);
@@ -365,7 +381,9 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const int akc = layoutA == GEMM_ROW_MAJOR;
     const int bkc = layoutB == GEMM_COL_MAJOR;
     dim3 grid((unsigned)tiles, 1, (unsigned)splits);
-    if (E.launch(p, in_dtype == GEMM_BF16, akc, bkc, grid, stream) != hipSuccess)
+    // the launcher's variant flag: bf16 among the 16-bit inputs, E5M2 among fp8
+    const int variant = (in_dtype == GEMM_BF16 || in_dtype == GEMM_FP8_E5M2) ? 1 : 0;
+    if (E.launch(p, variant, akc, bkc, grid, stream) != hipSuccess)
         return GEMM_ERR_HIP;
     if (splits > 1) {
         const int64_t total = M * N;

@@ -29,6 +29,14 @@ using CfgMediumI8 = TileCfg<128, 128, 128, 2, 2, 32, 4, 1>;
 using CfgSmallI8 = TileCfg<64, 64, 128, 2, 2, 32, 4, 1>;
 using CfgSkinnyI8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 1>;
 
+// OCP fp8 entries (E4M3 or E5M2 A and B): the same tiles in bytes, two
+// 16-byte chunks per lane and operand for v_mfma_scale_f32_32x32x64_f8f6f4 /
+// 16x16x128 (scales 2^0), so two MFMA steps per 128-byte K-tile.
+using CfgLarge8F8 = TileCfg<256, 256, 128, 2, 4, 32, 4, 1, 2>;
+using CfgMediumF8 = TileCfg<128, 128, 128, 2, 2, 32, 4, 1, 2>;
+using CfgSmallF8 = TileCfg<64, 64, 128, 2, 2, 32, 4, 1, 2>;
+using CfgSkinnyF8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 1, 2>;
+
 typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
                                 dim3 grid, hipStream_t stream);
 
@@ -54,6 +62,23 @@ hipError_t launch_large8_i8(const Params &, int, int, int, dim3, hipStream_t);
 hipError_t launch_medium_i8(const Params &, int, int, int, dim3, hipStream_t);
 hipError_t launch_small_i8(const Params &, int, int, int, dim3, hipStream_t);
 hipError_t launch_skinny_i8(const Params &, int, int, int, dim3, hipStream_t);
+
+// fp8 entries, one translation unit per (entry, format): kernels_<entry>_f8.hip
+// (E4M3) and kernels_<entry>_bf8.hip (E5M2); the bf flag of launch_fn selects
+// E5M2
+#define LIBGEMM_DECLARE_LAUNCH_F8(name)                                                  \
+    hipError_t launch_##name##_f8(const Params &, int, int, dim3, hipStream_t);        \
+    hipError_t launch_##name##_bf8(const Params &, int, int, dim3, hipStream_t);       \
+    inline hipError_t launch_##name##_fp8(const Params &p, int e5m2, int akc, int bkc,  \
+                                          dim3 grid, hipStream_t s) {                  \
+        return e5m2 ? launch_##name##_bf8(p, akc, bkc, grid, s)                         \
+                    : launch_##name##_f8(p, akc, bkc, grid, s);                         \
+    }
+LIBGEMM_DECLARE_LAUNCH_F8(large8)
+LIBGEMM_DECLARE_LAUNCH_F8(medium)
+LIBGEMM_DECLARE_LAUNCH_F8(small)
+LIBGEMM_DECLARE_LAUNCH_F8(skinny)
+#undef LIBGEMM_DECLARE_LAUNCH_F8
 
 template <class CF, int IT, bool AKC, bool BKC>
 hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {

@@ -52,8 +52,9 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 // dtype codes of the C ABI (C, D and out_dtype)
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3, DT_I32 = 4 };
-// input (A, B) element types of the kernels
-enum { IT_F16 = 0, IT_BF16 = 1, IT_I8 = 2 };
+// input (A, B) element types of the kernels: fp16, bf16, int8, OCP fp8 E4M3, E5M2
+enum { IT_F16 = 0, IT_BF16 = 1, IT_I8 = 2, IT_FP8 = 3, IT_BF8 = 4 };
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Keeps
 // every accumulator index a constant so the accumulators stay in registers.
@@ -101,20 +102,23 @@ struct Params {
 enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 
 // Block-tile configuration.  MF = 32 selects the 32x32 MFMA (32x32x16 for
-// 16-bit inputs, 32x32x32 for int8), 16 the 16x16 one (16x16x32, 16x16x64).
-// Waves form a WAVES_M x WAVES_N grid over the block tile.  ES is the input
-// element size in bytes; BK counts elements, so an LDS row holds BK*ES bytes.
-// Both MFMA shapes take 16 bytes of each operand per lane, so in bytes the
-// int8 and the 16-bit tiles have the same layout.
+// 16-bit inputs, 32x32x32 for int8, 32x32x64 for fp8), 16 the 16x16 one
+// (16x16x32, 16x16x64, 16x16x128).  Waves form a WAVES_M x WAVES_N grid over
+// the block tile.  ES is the input element size in bytes; BK counts
+// elements, so an LDS row holds BK*ES bytes.  FC is the number of 16-byte
+// chunks of each operand one lane holds per MFMA: 1 for the 16-bit and int8
+// MFMAs, 2 for the fp8 ones.  In bytes, the tiles of every type share one
+// LDS layout.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MF_, int GROUP_M_,
-          int ES_ = 2>
+          int ES_ = 2, int FC_ = 1>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
     static constexpr int MF = MF_;
     static constexpr int ES = ES_;
-    static constexpr int KSTEP = ((MF == 32) ? 32 : 64) / ES;  // k consumed by one MFMA
+    static constexpr int FC = FC_;
+    static constexpr int KSTEP = FC * ((MF == 32) ? 32 : 64) / ES;  // k consumed by one MFMA
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int TM = WTM / MF, TN = WTN / MF;
     static constexpr int CH = BK * ES / 16;  // 16-byte chunks per LDS row
@@ -436,7 +440,7 @@ struct LoaderRC {
 // int8: the accumulators hold int32 bit patterns in the same float vectors
 // (only moved, never used as floats until the epilogue reinterprets them).
 template <int IT>
-__device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
+__device__ __forceinline__ f32x16 mfma32_1(const u32x4 &a, const u32x4 &b, const f32x16 &c) {
     if constexpr (IT == IT_BF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -451,7 +455,7 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
 }
 
 template <int IT>
-__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+__device__ __forceinline__ f32x4 mfma16_1(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
     if constexpr (IT == IT_BF16)
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -463,6 +467,36 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f3
             f32x4, __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
                                                           __builtin_bit_cast(i32x4, b),
                                                           __builtin_bit_cast(i32x4, c), 0, 0, 0));
+}
+
+// fp8 operands: two 16-byte chunks per lane; scale exponents 127 (= 2^0).
+__device__ __forceinline__ i32x8 cat8(const u32x4 &lo, const u32x4 &hi) {
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+template <int IT, int FC>
+__device__ __forceinline__ f32x16 mfma32(const u32x4 (&af)[FC], const u32x4 (&bf)[FC],
+                                         const f32x16 &c) {
+    if constexpr (IT == IT_FP8 || IT == IT_BF8) {
+        constexpr int fmt = IT == IT_FP8 ? 0 : 1;
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            cat8(af[0], af[FC - 1]), cat8(bf[0], bf[FC - 1]), c, fmt, fmt, 0, 127, 0, 127);
+    } else {
+        return mfma32_1<IT>(af[0], bf[0], c);
+    }
+}
+
+template <int IT, int FC>
+__device__ __forceinline__ f32x4 mfma16(const u32x4 (&af)[FC], const u32x4 (&bf)[FC],
+                                        const f32x4 &c) {
+    if constexpr (IT == IT_FP8 || IT == IT_BF8) {
+        constexpr int fmt = IT == IT_FP8 ? 0 : 1;
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            cat8(af[0], af[FC - 1]), cat8(bf[0], bf[FC - 1]), c, fmt, fmt, 0, 127, 0, 127);
+    } else {
+        return mfma16_1<IT>(af[0], bf[0], c);
+    }
 }
 
 template <int MF> struct AccT;
@@ -762,8 +796,9 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN, THREADS = CF::THREADS;
     constexpr int KS = BK / CF::KSTEP;           // MFMA steps per K-tile
     constexpr int KCH = CF::KSTEP * CF::ES / 16;  // 16-byte LDS chunks per MFMA step
-    static_assert(KS % 2 == 0 && KS >= 4, "fragment slots alternate across K-tiles; the"
-                  " store, load and barrier steps are distinct");
+    static_assert(KS % 2 == 0 && KS >= 2, "fragment slots alternate across K-tiles; the"
+                  " store and barrier steps are distinct");
+    constexpr int FC = CF::FC;  // 16-byte chunks per lane and operand fragment
     // 8-bit operands always use K-contiguous chunks: the vector path needs
     // K-contiguous storage, the element-wise path gathers by layout
     static_assert(CF::ES == 2 || !VEC || (A_KC && B_KC), "int8 vector loads need K-contiguous A, B");
@@ -800,33 +835,45 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
 
     // Per-lane LDS byte offsets of each fragment at step 0; step s XORs in
     // s*KCH chunks (the chunk bits of s and of the lane never overlap).
+    // Lane l holds chunks (l / MF) * FC + c, c < FC, of each step; with
+    // FC = 2 the first of them is even, so chunk c sits at offset ^ 16*c.
+    static_assert(FC == 1 || FC == 2, "fragment chunks");
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
     uint32_t a_off[TM], b_off[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int r = wm * CF::WTM + i * MF + (lane & (MF - 1));
-        a_off[i] = (uint32_t)(r * CH + ((lane / MF) ^ swz(r))) * 16u;
+        a_off[i] = (uint32_t)(r * CH + (((lane / MF) * FC) ^ swz(r))) * 16u;
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int r = wn * CF::WTN + j * MF + (lane & (MF - 1));
-        b_off[j] = (uint32_t)(r * CH + ((lane / MF) ^ swz(r))) * 16u;
+        b_off[j] = (uint32_t)(r * CH + (((lane / MF) * FC) ^ swz(r))) * 16u;
     }
 
-    u32x4 fa[2][TM], fb[2][TN];
+    // With two chunks per fragment (fp8) the double-buffered fragments no
+    // longer fit next to the accumulators at two waves per SIMD, so the A
+    // fragments are single-buffered: A row i of the next step is read right
+    // after the last MFMA of row i in this step (B stays double-buffered).
+    constexpr bool A1 = FC == 2;
+    u32x4 fa[A1 ? 1 : 2][TM][FC], fb[2][TN][FC];
     // fragment f (A fragments first, then B) of step ks into slot sl
     auto read_one = [&](int buf, auto ks_tag, auto sl_tag, auto f_tag) {
         constexpr int ks = decltype(ks_tag)::value, sl = decltype(sl_tag)::value;
         constexpr int f = decltype(f_tag)::value;
         constexpr uint32_t kx = (uint32_t)(ks * KCH * 16);
-        if constexpr (f < TM) {
-            const char *ab = reinterpret_cast<const char *>(sA + buf * BM * CH);
-            fa[sl][f] = *reinterpret_cast<const u32x4 *>(ab + (a_off[f] ^ kx));
-        } else {
-            const char *bb = reinterpret_cast<const char *>(sB + buf * BN * CH);
-            fb[sl][f - TM] = *reinterpret_cast<const u32x4 *>(bb + (b_off[f - TM] ^ kx));
-        }
+        Unroll<0, FC>::run([&](auto c_tag) {
+            constexpr int c = decltype(c_tag)::value;
+            constexpr uint32_t cx = kx ^ (uint32_t)(16 * c);
+            if constexpr (f < TM) {
+                const char *ab = reinterpret_cast<const char *>(sA + buf * BM * CH);
+                fa[A1 ? 0 : sl][f][c] = *reinterpret_cast<const u32x4 *>(ab + (a_off[f] ^ cx));
+            } else {
+                const char *bb = reinterpret_cast<const char *>(sB + buf * BN * CH);
+                fb[sl][f - TM][c] = *reinterpret_cast<const u32x4 *>(bb + (b_off[f - TM] ^ cx));
+            }
+        });
     };
     auto mfma_one = [&](auto sl_tag, auto m_tag) {
         constexpr int sl = decltype(sl_tag)::value, m = decltype(m_tag)::value;
@@ -835,9 +882,9 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
         // the transposed tile, whose rows (D columns) land in consecutive
         // accumulator registers of one lane (see acc_col)
         if constexpr (MF == 32)
-            acc[i][j] = mfma32<IT>(fb[sl][j], fa[sl][i], acc[i][j]);
+            acc[i][j] = mfma32<IT, FC>(fb[sl][j], fa[A1 ? 0 : sl][i], acc[i][j]);
         else
-            acc[i][j] = mfma16<IT>(fb[sl][j], fa[sl][i], acc[i][j]);
+            acc[i][j] = mfma16<IT, FC>(fb[sl][j], fa[A1 ? 0 : sl][i], acc[i][j]);
     };
     auto store_one = [&](int buf, auto w_tag) {
         constexpr int w = decltype(w_tag)::value;
@@ -933,19 +980,28 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
                 // its first MFMAs need A0 and all of B at once), one per MFMA
                 // from the start of the step, or spread evenly when there are
                 // more fragments than MFMAs
-                constexpr int r_lo = NR <= NM ? (m < NR ? m : NR) : m * NR / NM;
-                constexpr int r_hi = NR <= NM ? (m < NR ? m + 1 : NR) : (m + 1) * NR / NM;
-                Unroll<r_lo, r_hi>::run([&](auto q_tag) {
-                    constexpr int q = decltype(q_tag)::value;
-                    constexpr int fid = (q == 0) ? 0 : (q <= TN ? TM + q - 1 : q - TN);
-                    const auto f = std::integral_constant<int, fid>{};
+                auto read_next = [&](auto f) {
                     if constexpr (ks + 1 < KS)
                         read_one(cur, std::integral_constant<int, ks + 1>{},
                                  std::integral_constant<int, sl ^ 1>{}, f);
                     else
                         read_one(cur ^ 1, std::integral_constant<int, 0>{},
                                  std::integral_constant<int, 0>{}, f);
-                });
+                };
+                if constexpr (A1) {
+                    // B column m after MFMA m (m < TN); A row i after its last MFMA
+                    if constexpr (m < TN) read_next(std::integral_constant<int, TM + m>{});
+                    if constexpr (m % TN == TN - 1)
+                        read_next(std::integral_constant<int, m / TN>{});
+                } else {
+                    constexpr int r_lo = NR <= NM ? (m < NR ? m : NR) : m * NR / NM;
+                    constexpr int r_hi = NR <= NM ? (m < NR ? m + 1 : NR) : (m + 1) * NR / NM;
+                    Unroll<r_lo, r_hi>::run([&](auto q_tag) {
+                        constexpr int q = decltype(q_tag)::value;
+                        constexpr int fid = (q == 0) ? 0 : (q <= TN ? TM + q - 1 : q - TN);
+                        read_next(std::integral_constant<int, fid>{});
+                    });
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         });

@@ -31,11 +31,20 @@ import numpy as np
 import torch
 
 F32, F16, BF16 = 0, 1, 2
+FP8_E4M3, FP8_E5M2 = 5, 6
 ROW_MAJOR, COL_MAJOR = 0, 1
 
 NAN16 = {F16: 0x7E00, BF16: 0x7FC0}
+NAN8 = {FP8_E4M3: 0x7F, FP8_E5M2: 0x7E}
 SENTINEL_F32 = np.float32(-12345.5)
 SENTINEL_16 = np.uint16(0x5A5A)
+
+
+def to_bits8(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round float32 values to OCP fp8 (E4M3 or E5M2, torch's conversion) -> uint8 bits."""
+    dt = torch.float8_e4m3fn if dtype == FP8_E4M3 else torch.float8_e5m2
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dt)
+    return t.view(torch.uint8).numpy()
 
 
 def to_bits16(x: np.ndarray, dtype: int) -> np.ndarray:
@@ -101,7 +110,13 @@ class Problem:
 
 
 def _operand(rng, rows: int, cols: int, ld: int, dtype: int, values: str) -> np.ndarray:
-    """A (rows, ld) uint16 buffer whose first `cols` columns hold values, pad = NaN."""
+    """A (rows, ld) buffer of 16-bit (uint16) or fp8 (uint8) patterns whose
+    first `cols` columns hold values, pad = NaN."""
+    if dtype in NAN8:
+        buf = np.full((rows, ld), NAN8[dtype], dtype=np.uint8)
+        if rows and cols:
+            buf[:, :cols] = to_bits8(_draw(rng, (rows, cols), values), dtype)
+        return buf
     buf = np.full((rows, ld), NAN16[dtype], dtype=np.uint16)
     if rows and cols:
         buf[:, :cols] = to_bits16(_draw(rng, (rows, cols), values), dtype)

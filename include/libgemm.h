@@ -18,6 +18,9 @@
  *    section "WMMA API解释" item (5) mma_sync.
  *  - fp16-accumulate HGEMM variant (fp16 A, B, C, D):
  *    "hgemm_mma_m16n8k16_naive_kernel", section 1.1 "m16n8k16 指令规格".
+ *  - 8-bit float inputs (fp8): the per-architecture precision lists of
+ *    "深入CUDA Tensor Core与WMMA…", section 2.3; here the OCP E4M3 and E5M2
+ *    formats gfx950's matrix cores take.
  *  - int8 inputs with an int32 accumulator: the fragment type lists of
  *    "CUDA算子优化(5)：WMMA矩阵乘法" (char operands, int accumulator) and
  *    "深入CUDA Tensor Core与WMMA…", section 2.3 (INT8 on the matrix units).
@@ -58,7 +61,9 @@ typedef enum {
     GEMM_F16 = 1,  /* IEEE binary16 */
     GEMM_BF16 = 2, /* bfloat16 (upper half of binary32) */
     GEMM_I8 = 3,   /* two's-complement 8-bit integer (A, B)  */
-    GEMM_I32 = 4   /* two's-complement 32-bit integer (C, D, accumulator) */
+    GEMM_I32 = 4,  /* two's-complement 32-bit integer (C, D, accumulator) */
+    GEMM_FP8_E4M3 = 5, /* OCP 8-bit float E4M3 (A, B): bias 7, max 448, NaN, no Inf */
+    GEMM_FP8_E5M2 = 6  /* OCP 8-bit float E5M2 (A, B): bias 15, IEEE-style Inf/NaN */
 } gemm_dtype_t;
 
 /* Return codes.  GEMM_OK means "validated and enqueued". */
@@ -89,8 +94,9 @@ typedef enum {
  *                may be NULL (C = 0).  C == D with ldc == ldd is the in-place
  *                update C = A x B + C; any other overlap of C and D is rejected.
  *   D, ldd       device pointer to out_dtype elements, row-major, ldd >= N.
- *   in_dtype     GEMM_F16, GEMM_BF16, or GEMM_I8 (A and B int8).
- *   acc_dtype    GEMM_F32 (out_dtype F32, F16 or BF16), or GEMM_F16 with
+ *   in_dtype     GEMM_F16, GEMM_BF16, GEMM_FP8_E4M3, GEMM_FP8_E5M2 (A and B
+ *                both of that type), or GEMM_I8 (A and B int8).
+ *   acc_dtype    GEMM_F32 (out_dtype F32, F16 or BF16; any float input), or GEMM_F16 with
  *                in_dtype == out_dtype == GEMM_F16 (HGEMM), or GEMM_I32 with
  *                in_dtype GEMM_I8 and out_dtype GEMM_I32.
  *   out_dtype    dtype of C and D.
@@ -113,8 +119,13 @@ typedef enum {
  *
  * Speed: 16-byte vector loads are used where A and B base pointers are
  * 16-byte aligned and lda, ldb are multiples of 16 bytes (the pages' ldm
- * rule), for int8 only with A row-major and B column-major (both
+ * rule), for int8 and fp8 only with A row-major and B column-major (both
  * K-contiguous); anything else runs correct element-wise loads.
+ *
+ * fp8 accuracy: gfx950's fp8 MFMA adds each block of 64 products (per
+ * output) with a relative precision of about 2^-14 of the block's largest
+ * product (measured), before the fp32 accumulation; products of inputs of
+ * similar magnitude, and integer-valued inputs, come out exact.
  */
 int gemm_run(int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda, int layoutA,

@@ -1,0 +1,104 @@
+"""GPU parity of OCP fp8 inputs (E4M3, E5M2; fp32 accumulate) through the C ABI
+against the oracle.  Integer-valued inputs are bit-exact; other data is held
+to the plain tolerance plus the fp8 MFMA's block term (gpu_util.fp8_block_bound)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import dense_mixed_precision_tiled_amd as lg
+import oracle
+from dense_mixed_precision_tiled_amd import workloads as W
+from dense_mixed_precision_tiled_amd.workloads import (BF16, COL_MAJOR, F16, F32, FP8_E4M3,
+                                                       FP8_E5M2, ROW_MAJOR)
+from gpu_util import DeviceProblem, compare, log, oracle_full, oracle_samples, region
+
+pytestmark = pytest.mark.gpu
+
+# fp8 tile-table entries -> block tile edge (None: skinny split-K)
+F8_ENTRY_TILE = {9: 256, 10: 128, 11: 64, 12: None}
+
+
+def _shape(cid):
+    bm = F8_ENTRY_TILE[cid]
+    return (13, 3 * 128 - 5, 2200) if bm is None else (2 * bm + 17, 3 * bm - 5, 400)
+
+
+def _check(prob, exact, config=None, label=""):
+    log("case: %s config=%s" % (label, config))
+    dp = DeviceProblem(prob)
+    dp.run(config=config)
+    got = dp.result()
+    ref = oracle_full(prob)
+    compare(prob, region(prob, got), region(prob, ref), exact, label=label)
+
+
+@pytest.mark.parametrize("cid", sorted(F8_ENTRY_TILE))
+@pytest.mark.parametrize("fmt", [FP8_E4M3, FP8_E5M2])
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, COL_MAJOR), (ROW_MAJOR, ROW_MAJOR),
+                                   (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)])
+def test_every_fp8_entry_format_layout(cid, fmt, la, lb):
+    M, N, K = _shape(cid)
+    for values, exact in (("int", True), ("uniform", False)):
+        prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, in_dtype=fmt, values=values,
+                              c_values="normal" if values == "uniform" else "int",
+                              ldd=N + 3, seed=9000 + cid + 10 * fmt)
+        _check(prob, exact, cid, "fp8 cfg%d fmt%d A%d B%d %s" % (cid, fmt, la, lb, values))
+
+
+@pytest.mark.parametrize("cid", sorted(F8_ENTRY_TILE))
+def test_fp8_output_modes(cid):
+    M, N, K = _shape(cid)
+    modes = [dict(out_dtype=F16, c_values="uniform", ldd=N + 3, satf=1),
+             dict(out_dtype=BF16, c_values="normal", ldd=N + 8),
+             dict(out_dtype=F32, c_values="normal", inplace=True, ldd=N + 5)]
+    for mode in modes:
+        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=FP8_E4M3,
+                              values="normal", seed=9100 + cid, **mode)
+        _check(prob, False, cid, "fp8 cfg%d out=%d" % (cid, prob.out_dtype))
+
+
+def test_fp8_unaligned_and_small_shapes():
+    for shape in ((1, 1, 1), (17, 33, 65), (70, 45, 0), (100, 90, 300)):
+        M, N, K = shape
+        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=FP8_E5M2,
+                              values="int", c_values="int", lda=K + 1, ldd=N + 2,
+                              seed=9200 + M)
+        _check(prob, True, None, "fp8 %dx%dx%d unaligned lda" % shape)
+
+
+def test_fp8_with_the_extended_epilogue():
+    M, N, K = 300, 260, 256
+    prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=FP8_E4M3,
+                          values="int", seed=9300)
+    dp = DeviceProblem(prob)
+    bias = torch.arange(N, dtype=torch.float32, device="cuda") - N / 2
+    Dc = torch.zeros((N, M), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    epi = lg.GemmEpilogue(alpha=0.5, beta=1.0, bias=bias.data_ptr(),
+                          activation=lg.GEMM_ACT_RELU, layoutD=COL_MAJOR)
+    st = lg.gemm_run_ex(M, N, K, dp.A.data_ptr(), prob.lda, prob.layoutA, dp.B.data_ptr(),
+                        prob.ldb, prob.layoutB, None, N, Dc.data_ptr(), M, FP8_E4M3, F32, F32, 0,
+                        epi, s)
+    assert st == 0
+    torch.cuda.synchronize()
+    ref = np.zeros(N * M, dtype=np.float32)
+    oracle.gemm_ex(M, N, K, prob.A.ravel(), prob.lda, prob.layoutA, prob.B.ravel(), prob.ldb,
+                   prob.layoutB, None, N, ROW_MAJOR, ref, M, COL_MAJOR, FP8_E4M3, F32, F32, 0,
+                   0.5, 1.0, bias.cpu().numpy(), oracle.ACT_RELU)
+    assert np.array_equal(Dc.cpu().numpy().ravel(), ref)
+
+
+@pytest.mark.parametrize("fmt", [FP8_E4M3, FP8_E5M2])
+def test_4096_fp8_sampled(fmt):
+    n = 4096
+    prob = W.make_problem(n, n, n, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=fmt,
+                          values="uniform", seed=9400 + fmt)
+    log("case: fp8 4096^3 fmt %d" % fmt)
+    dp = DeviceProblem(prob)
+    dp.run()
+    got = dp.result()
+    rows, cols = W.sample_indices(n, n, 4096, seed=9401)
+    compare(prob, got[rows, cols], oracle_samples(prob, rows, cols), False, rows=rows,
+            cols=cols, label="fp8 4096 sampled")

@@ -134,10 +134,13 @@ def _entry_shapes():
 
 
 def test_config_ids_match_table():
-    # 16-bit entries here; the int8 entries (ids 5..8) are covered by test_int8_gpu
-    assert lg.gemm_num_configs() == len(ENTRY_TILE) + 4
-    for cid in range(len(ENTRY_TILE), lg.gemm_num_configs()):
+    # 16-bit entries here; the int8 entries (ids 5..8) and the fp8 entries
+    # (ids 9..12) are covered by test_int8_gpu and test_fp8_gpu
+    assert lg.gemm_num_configs() == len(ENTRY_TILE) + 8
+    for cid in range(5, 9):
         assert lg.gemm_config_name(cid).startswith("i8_")
+    for cid in range(9, 13):
+        assert lg.gemm_config_name(cid).startswith("fp8_")
     for cid, bm in ENTRY_TILE.items():
         name = lg.gemm_config_name(cid)
         if bm is None:
