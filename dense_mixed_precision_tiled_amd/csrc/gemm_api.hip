@@ -68,8 +68,8 @@ const Entry kTable[] = {
      launch_small_i8},
     {"i8_skinny_16x128x256_w1x4_mfma16x16x64_splitk", CfgSkinnyI8::BM, CfgSkinnyI8::BN,
      CfgSkinnyI8::BK, 1, 1, launch_skinny_i8},
-    {"fp8_large8_256x256x128_w2x4_mfma32x32x64", CfgLarge8F8::BM, CfgLarge8F8::BN,
-     CfgLarge8F8::BK, 0, 2, launch_large8_fp8},
+    {"fp8_large_256x256x128_w2x2_mfma32x32x64", CfgLargeF8::BM, CfgLargeF8::BN,
+     CfgLargeF8::BK, 0, 2, launch_large_fp8},
     {"fp8_medium_128x128x128_w2x2_mfma32x32x64", CfgMediumF8::BM, CfgMediumF8::BN,
      CfgMediumF8::BK, 0, 2, launch_medium_fp8},
     {"fp8_small_64x64x128_w2x2_mfma32x32x64", CfgSmallF8::BM, CfgSmallF8::BN, CfgSmallF8::BK, 0,
@@ -80,7 +80,7 @@ const Entry kTable[] = {
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
 enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
        CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8,
-       CFG_F8_LARGE8 = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12 };
+       CFG_F8_LARGE = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12 };
 
 bool is_fp8(int in_dtype) { return in_dtype == GEMM_FP8_E4M3 || in_dtype == GEMM_FP8_E5M2; }
 int input_class(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : (is_fp8(in_dtype) ? 2 : 0); }
@@ -196,7 +196,7 @@ int select_config(int64_t M, int64_t N, int64_t K, int klass) {
     static const int kByClass[3][4] = {
         {CFG_SKINNY, CFG_LARGE8, CFG_MEDIUM, CFG_SMALL},
         {CFG_I8_SKINNY, CFG_I8_LARGE8, CFG_I8_MEDIUM, CFG_I8_SMALL},
-        {CFG_F8_SKINNY, CFG_F8_LARGE8, CFG_F8_MEDIUM, CFG_F8_SMALL}};
+        {CFG_F8_SKINNY, CFG_F8_LARGE, CFG_F8_MEDIUM, CFG_F8_SMALL}};
     const int *e = kByClass[klass];
     if (M <= CfgSkinny::BM) return e[0];
     const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
