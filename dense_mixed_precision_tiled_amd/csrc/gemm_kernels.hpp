@@ -1050,9 +1050,19 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     // split-K slices, unaligned or column-major C, and the extended epilogue
     // (scale, bias, activation) -- stages the tile through LDS one MF-row block
     // at a time and finishes it in a loop that is not unrolled, so the
-    // extended arithmetic is instantiated once.
+    // extended arithmetic is instantiated once.  There, groups that lie inside
+    // M x N still use vector loads and stores; only groups that cross the
+    // edge, or unaligned / column-major C and D, go element by element.
     constexpr int NG = AccT<MF>::N / 4;  // 4-column groups per MFMA tile and lane
     const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.cd_vec && p.splits == 1;
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
+    // the register path also takes aligned edge tiles: each group checks
+    // whether it lies inside M x N (vector finish), crosses the edge
+    // (element-wise) or lies outside (nothing to store).  Only for wave tiles
+    // of at most 32 groups per lane: unrolled over 64 groups the checks make
+    // a translation unit compile for minutes; larger wave tiles send edge
+    // tiles through the staged loop.
+    constexpr bool EDGE_DIRECT = TM * TN * NG <= 32;
     auto direct = [&](auto out_tag) {
         constexpr int OUT = decltype(out_tag)::value;
         Unroll<0, TM>::run([&](auto ii) {
@@ -1065,17 +1075,28 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                     const int col = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
                     const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    finish4<OUT, true, false>(p, row, col, v);
+                    if constexpr (EDGE_DIRECT) {
+                        if (interior || (row < p.M && col + 4 <= p.N))
+                            finish4<OUT, true, false>(p, row, col, v);
+                        else
+                            finish4<OUT, false, false>(p, row, col, v);
+                    } else {
+                        finish4<OUT, true, false>(p, row, col, v);
+                    }
                 });
             });
         });
     };
-    if (full && !p.epi) {
-        if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{});
-        else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
-        else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
-        else direct(std::integral_constant<int, DT_BF16>{});
-        return;
+    // (kernels with element-wise operand loads serve unaligned operands, a
+    // slow path anyway: they finish through the staged loop only)
+    if constexpr (VEC) {
+        if (p.cd_vec && p.splits == 1 && !p.epi && (EDGE_DIRECT || interior)) {
+            if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{});
+            else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
+            else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
+            else direct(std::integral_constant<int, DT_BF16>{});
+            return;
+        }
     }
     // staged path: one MF-row block per wave at a time in the wave's own LDS
     // region (free: the K loop's last barrier has passed), rows padded
@@ -1111,19 +1132,28 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
             for (int rr = lane / LPR; rr < MF; rr += RPP) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + rr * SROW + c4);
                 const int gi = row0 + i * MF + rr, gj = col0 + c4;
+                // a group inside M x N of an edge tile still takes the vector
+                // finish (C, D and bias alignment are tile-independent)
+                const bool gfull = full || (p.cd_vec && p.splits == 1 && gi < p.M && gj + 4 <= p.N);
                 if (p.splits > 1) {
                     finish4<-1, false, false>(p, gi, gj, v);
                 } else if constexpr (IT == IT_I8) {  // int32 out, plain epilogue only
-                    if (full) finish4<DT_I32, true, false>(p, gi, gj, v);
+                    if (gfull) finish4<DT_I32, true, false>(p, gi, gj, v);
                     else finish4<DT_I32, false, false>(p, gi, gj, v);
-                } else if (full) {  // interior tile, extended epilogue
-                    if (p.out_dtype == DT_F32) finish4<DT_F32, true, true>(p, gi, gj, v);
-                    else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true>(p, gi, gj, v);
-                    else finish4<DT_BF16, true, true>(p, gi, gj, v);
                 } else if (p.epi) {
-                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, true>(p, gi, gj, v);
-                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true>(p, gi, gj, v);
-                    else finish4<DT_BF16, false, true>(p, gi, gj, v);
+                    if (gfull) {
+                        if (p.out_dtype == DT_F32) finish4<DT_F32, true, true>(p, gi, gj, v);
+                        else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true>(p, gi, gj, v);
+                        else finish4<DT_BF16, true, true>(p, gi, gj, v);
+                    } else {
+                        if (p.out_dtype == DT_F32) finish4<DT_F32, false, true>(p, gi, gj, v);
+                        else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true>(p, gi, gj, v);
+                        else finish4<DT_BF16, false, true>(p, gi, gj, v);
+                    }
+                } else if (gfull) {
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, true, false>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, true, false>(p, gi, gj, v);
+                    else finish4<DT_BF16, true, false>(p, gi, gj, v);
                 } else {
                     if (p.out_dtype == DT_F32) finish4<DT_F32, false, false>(p, gi, gj, v);
                     else if (p.out_dtype == DT_F16) finish4<DT_F16, false, false>(p, gi, gj, v);
