@@ -645,7 +645,24 @@ __device__ __forceinline__ float from_out16(uint32_t h) {
 // result rounded once to OUT, satf applied and the group stored.  FULL: the
 // group lies inside M x N and C/D/bias allow 4-element vector access, so no
 // checks; else each element is checked and stored alone.
-template <int OUT, bool FULL, bool EPI>
+// C(i, j..j+3) of a group inside M x N with vector-friendly row-major C, as
+// fp32 values (float outputs only).
+template <int OUT>
+__device__ __forceinline__ f32x4 load_c4(const Params &p, int i, int j) {
+    if constexpr (OUT == DT_F32) {
+        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.C) +
+                                                (int64_t)i * p.ldc + j);
+    } else {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(
+            reinterpret_cast<const uint16_t *>(p.C) + (int64_t)i * p.ldc + j);
+        return f32x4{from_out16<OUT>(lo16(w[0])), from_out16<OUT>(hi16(w[0])),
+                     from_out16<OUT>(lo16(w[1])), from_out16<OUT>(hi16(w[1]))};
+    }
+}
+
+// CADDED: the plain epilogue's C has already been added to v (the register
+// epilogue loads C for a whole row block ahead of its stores).
+template <int OUT, bool FULL, bool EPI, bool CADDED = false>
 __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) {
     const int nval = FULL ? 4 : min(p.N - j, 4);
     if (!FULL && (i >= p.M || nval <= 0)) return;
@@ -699,7 +716,7 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
             return c;
         };
         if constexpr (!EPI) {
-            if (p.C) {
+            if (!CADDED && p.C) {
                 if (FULL) {
                     v += c4();
                 } else {
@@ -1065,23 +1082,41 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     constexpr bool EDGE_DIRECT = TM * TN * NG <= 32;
     auto direct = [&](auto out_tag) {
         constexpr int OUT = decltype(out_tag)::value;
+        // Float outputs load C for a whole row block before the block's
+        // stores: a wait for a load also waits for every earlier store, so
+        // per-group loads would serialise the block.
+        constexpr bool PRE = OUT != DT_I32;
         Unroll<0, TM>::run([&](auto ii) {
             constexpr int i = decltype(ii)::value;
             const int row = m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane);
+            auto col_of = [&](int j, int g) {
+                return n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
+            };
+            auto inside = [&](int col) {
+                return !EDGE_DIRECT || interior || (row < p.M && col + 4 <= p.N);
+            };
+            f32x4 cpre[TN][NG];
+            if constexpr (PRE) {
+                Unroll<0, TN>::run([&](auto jj) {
+                    Unroll<0, NG>::run([&](auto gg) {
+                        constexpr int j = decltype(jj)::value, g = decltype(gg)::value;
+                        cpre[j][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        if (p.C && inside(col_of(j, g))) cpre[j][g] = load_c4<OUT>(p, row, col_of(j, g));
+                    });
+                });
+            }
             Unroll<0, TN>::run([&](auto jj) {
                 constexpr int j = decltype(jj)::value;
                 Unroll<0, NG>::run([&](auto gg) {
                     constexpr int g = decltype(gg)::value;
-                    const int col = n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
+                    const int col = col_of(j, g);
                     const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    if constexpr (EDGE_DIRECT) {
-                        if (interior || (row < p.M && col + 4 <= p.N))
-                            finish4<OUT, true, false>(p, row, col, v);
-                        else
-                            finish4<OUT, false, false>(p, row, col, v);
-                    } else {
-                        finish4<OUT, true, false>(p, row, col, v);
+                    if (inside(col)) {
+                        if constexpr (PRE) finish4<OUT, true, false, true>(p, row, col, v + cpre[j][g]);
+                        else finish4<OUT, true, false>(p, row, col, v);
+                    } else if constexpr (EDGE_DIRECT) {
+                        finish4<OUT, false, false>(p, row, col, v);
                     }
                 });
             });
