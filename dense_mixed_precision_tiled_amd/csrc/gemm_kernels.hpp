@@ -1072,14 +1072,11 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     // edge, or unaligned / column-major C and D, go element by element.
     constexpr int NG = AccT<MF>::N / 4;  // 4-column groups per MFMA tile and lane
     const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.cd_vec && p.splits == 1;
-    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
-    // the register path also takes aligned edge tiles: each group checks
-    // whether it lies inside M x N (vector finish), crosses the edge
-    // (element-wise) or lies outside (nothing to store).  Only for wave tiles
-    // of at most 32 groups per lane: unrolled over 64 groups the checks make
-    // a translation unit compile for minutes; larger wave tiles send edge
-    // tiles through the staged loop.
-    constexpr bool EDGE_DIRECT = TM * TN * NG <= 32;
+    // (Edge tiles go through the staged loop below, which stores every group
+    // inside M x N with vector stores too.  Handling them here, with a bounds
+    // check and an element-wise fallback per group, made this unrolled code
+    // three times larger: that cost int8 20% (epilogue spills) and the
+    // 16384^2 x 1024 shape, 16 tiles per CU, 25%.)
     auto direct = [&](auto out_tag) {
         constexpr int OUT = decltype(out_tag)::value;
         // Float outputs load C for a whole row block before the block's
@@ -1092,16 +1089,13 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
             auto col_of = [&](int j, int g) {
                 return n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
             };
-            auto inside = [&](int col) {
-                return !EDGE_DIRECT || interior || (row < p.M && col + 4 <= p.N);
-            };
             f32x4 cpre[TN][NG];
             if constexpr (PRE) {
                 Unroll<0, TN>::run([&](auto jj) {
                     Unroll<0, NG>::run([&](auto gg) {
                         constexpr int j = decltype(jj)::value, g = decltype(gg)::value;
                         cpre[j][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        if (p.C && inside(col_of(j, g))) cpre[j][g] = load_c4<OUT>(p, row, col_of(j, g));
+                        if (p.C) cpre[j][g] = load_c4<OUT>(p, row, col_of(j, g));
                     });
                 });
             }
@@ -1112,12 +1106,8 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                     const int col = col_of(j, g);
                     const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                      acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    if (inside(col)) {
-                        if constexpr (PRE) finish4<OUT, true, false, true>(p, row, col, v + cpre[j][g]);
-                        else finish4<OUT, true, false>(p, row, col, v);
-                    } else if constexpr (EDGE_DIRECT) {
-                        finish4<OUT, false, false>(p, row, col, v);
-                    }
+                    if constexpr (PRE) finish4<OUT, true, false, true>(p, row, col, v + cpre[j][g]);
+                    else finish4<OUT, true, false>(p, row, col, v);
                 });
             });
         });
@@ -1125,7 +1115,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     // (kernels with element-wise operand loads serve unaligned operands, a
     // slow path anyway: they finish through the staged loop only)
     if constexpr (VEC) {
-        if (p.cd_vec && p.splits == 1 && !p.epi && (EDGE_DIRECT || interior)) {
+        if (full && !p.epi) {
             if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{});
             else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
             else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
