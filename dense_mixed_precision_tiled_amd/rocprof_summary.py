@@ -16,10 +16,10 @@ Two subcommands, both reading the CSV files rocprofv3 writes with
             so that bench.py reports it only while the kernels are unchanged.
 
     python -m dense_mixed_precision_tiled_amd.rocprof_summary stats \\
-        --csv gpurun_out/prof/bench_kernel_stats.csv --command "..." --out profiles/x.md
+        --csv OUT/prof/bench_kernel_stats.csv --command "..." --out profiles/x.md
     python -m dense_mixed_precision_tiled_amd.rocprof_summary traffic \\
-        --fetch gpurun_out/pmc_fetch/fetch_counter_collection.csv \\
-        --write gpurun_out/pmc_write/write_counter_collection.csv \\
+        --fetch OUT/pmc_fetch/fetch_counter_collection.csv \\
+        --write OUT/pmc_write/write_counter_collection.csv \\
         --copy-bytes 268435456 --command "..." --out profiles/traffic_gemm_4096_f16.json
 """
 from __future__ import annotations
