@@ -660,8 +660,10 @@ __device__ __forceinline__ f32x4 load_c4(const Params &p, int i, int j) {
     }
 }
 
-// CADDED: the plain epilogue's C has already been added to v (the register
-// epilogue loads C for a whole row block ahead of its stores).
+// CADDED: the linear part of the epilogue is already in v -- C for the plain
+// epilogue, alpha * sum + beta * C + bias for the extended one (both epilogue
+// paths load these for a whole row block ahead of its stores); only the
+// activation, rounding, satf and store remain.
 template <int OUT, bool FULL, bool EPI, bool CADDED = false>
 __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) {
     const int nval = FULL ? 4 : min(p.N - j, 4);
@@ -723,7 +725,7 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
                     for (int e = 0; e < nval; ++e) v[e] += load_c(p, i, j + e);
                 }
             }
-        } else {
+        } else if constexpr (!CADDED) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = p.alpha * v[e];
             if (p.C) {
@@ -746,6 +748,9 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = activate(v[e], p.act);
             }
+        } else if (p.act != ACT_NONE) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = activate(v[e], p.act);
         }
         const int64_t off = (int64_t)i * p.ldd + j;
         if constexpr (OUT == DT_F32) {
@@ -1131,12 +1136,71 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         constexpr int SROW = WTN + 8;          // floats per staged row
         constexpr int LPR = WTN / 4;           // lanes per staged row
         constexpr int RPP = 64 / LPR;          // rows per pass of the wave
-        static_assert(64 % LPR == 0, "lanes per staged row");
+        constexpr int PASSES = MF / RPP;       // passes per row block
+        constexpr int QB = PASSES < 8 ? PASSES : 8;  // passes whose loads are in flight together
+        static_assert(64 % LPR == 0 && PASSES % QB == 0, "lanes per staged row");
         static_assert(CF::WAVES_M * CF::WAVES_N * MF * SROW * 4 <= (int)sizeof(smem),
                       "staging fits in the operand buffers");
         float *stage = reinterpret_cast<float *>(smem) + wave * MF * SROW;
         const int row0 = m0 + wm * CF::WTM, col0 = n0 + wn * WTN;
-        const int c4 = (lane % LPR) * 4;
+        const int c4 = (lane % LPR) * 4, gj = col0 + c4;
+        const bool gin = gj + 4 <= p.N;
+        // group (gi, gj..gj+3) inside M x N with vector-friendly C, D and bias
+        auto gfull_at = [&](int gi) { return full || (p.cd_vec && p.splits == 1 && gi < p.M && gin); };
+        // Linear part of the epilogue (alpha * sum + beta * C + bias, or sum + C)
+        // applied to the staged row block in place, with all its C and bias loads
+        // issued before any of its stores: on gfx9 a wait for a load also waits
+        // for every earlier store, so loading per group would serialise the
+        // stores.  (int32 outputs add C in 64 bits at the store instead.)
+        auto linear = [&](auto out_tag, int i) {
+            constexpr int OUT = decltype(out_tag)::value;
+            f32x4 bcol = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.epi && p.bias && !p.bias_rows) {
+                if (p.cd_vec && gin) {
+                    bcol = *reinterpret_cast<const f32x4 *>(p.bias + gj);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (gj + e < p.N) bcol[e] = p.bias[gj + e];
+                }
+            }
+#pragma nounroll
+            for (int q0 = 0; q0 < PASSES; q0 += QB) {
+                f32x4 cv[QB];
+                float brow[QB];
+                Unroll<0, QB>::run([&](auto qq) {
+                    constexpr int q = decltype(qq)::value;
+                    const int gi = row0 + i * MF + lane / LPR + (q0 + q) * RPP;
+                    cv[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    brow[q] = 0.0f;
+                    if (p.C) {
+                        if (gfull_at(gi)) {
+                            cv[q] = load_c4<OUT>(p, gi, gj);
+                        } else if (gi < p.M) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (gj + e < p.N) cv[q][e] = load_c(p, gi, gj + e);
+                        }
+                    }
+                    if (p.epi && p.bias && p.bias_rows && gi < p.M) brow[q] = p.bias[gi];
+                });
+                Unroll<0, QB>::run([&](auto qq) {
+                    constexpr int q = decltype(qq)::value;
+                    f32x4 *sp = reinterpret_cast<f32x4 *>(
+                        stage + (lane / LPR + (q0 + q) * RPP) * SROW + c4);
+                    f32x4 v = *sp;
+                    if (p.epi) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = p.alpha * v[e];
+                        if (p.C) v += p.beta * cv[q];
+                        if (p.bias) v += p.bias_rows ? f32x4{brow[q], brow[q], brow[q], brow[q]} : bcol;
+                    } else {
+                        v += cv[q];
+                    }
+                    *sp = v;
+                });
+            }
+        };
 #pragma nounroll
         for (int i = 0; i < TM; ++i) {
             // stage row block i (constant accumulator indices in each case)
@@ -1154,12 +1218,22 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                     });
                 });
             });
+            // (LDS operations of one wave complete in order; this only keeps
+            // the compiler from moving the reads above the writes)
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (IT != IT_I8) {
+                if (p.splits == 1 && (p.C || p.epi)) {
+                    if (p.out_dtype == DT_F32) linear(std::integral_constant<int, DT_F32>{}, i);
+                    else if (p.out_dtype == DT_F16) linear(std::integral_constant<int, DT_F16>{}, i);
+                    else linear(std::integral_constant<int, DT_BF16>{}, i);
+                }
+            }
             for (int rr = lane / LPR; rr < MF; rr += RPP) {
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(stage + rr * SROW + c4);
-                const int gi = row0 + i * MF + rr, gj = col0 + c4;
+                const int gi = row0 + i * MF + rr;
                 // a group inside M x N of an edge tile still takes the vector
                 // finish (C, D and bias alignment are tile-independent)
-                const bool gfull = full || (p.cd_vec && p.splits == 1 && gi < p.M && gj + 4 <= p.N);
+                const bool gfull = gfull_at(gi);
                 if (p.splits > 1) {
                     finish4<-1, false, false>(p, gi, gj, v);
                 } else if constexpr (IT == IT_I8) {  // int32 out, plain epilogue only
@@ -1167,24 +1241,25 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                     else finish4<DT_I32, false, false>(p, gi, gj, v);
                 } else if (p.epi) {
                     if (gfull) {
-                        if (p.out_dtype == DT_F32) finish4<DT_F32, true, true>(p, gi, gj, v);
-                        else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true>(p, gi, gj, v);
-                        else finish4<DT_BF16, true, true>(p, gi, gj, v);
+                        if (p.out_dtype == DT_F32) finish4<DT_F32, true, true, true>(p, gi, gj, v);
+                        else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true, true>(p, gi, gj, v);
+                        else finish4<DT_BF16, true, true, true>(p, gi, gj, v);
                     } else {
-                        if (p.out_dtype == DT_F32) finish4<DT_F32, false, true>(p, gi, gj, v);
-                        else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true>(p, gi, gj, v);
-                        else finish4<DT_BF16, false, true>(p, gi, gj, v);
+                        if (p.out_dtype == DT_F32) finish4<DT_F32, false, true, true>(p, gi, gj, v);
+                        else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true, true>(p, gi, gj, v);
+                        else finish4<DT_BF16, false, true, true>(p, gi, gj, v);
                     }
                 } else if (gfull) {
-                    if (p.out_dtype == DT_F32) finish4<DT_F32, true, false>(p, gi, gj, v);
-                    else if (p.out_dtype == DT_F16) finish4<DT_F16, true, false>(p, gi, gj, v);
-                    else finish4<DT_BF16, true, false>(p, gi, gj, v);
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, true, false, true>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, true, false, true>(p, gi, gj, v);
+                    else finish4<DT_BF16, true, false, true>(p, gi, gj, v);
                 } else {
-                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, false>(p, gi, gj, v);
-                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, false>(p, gi, gj, v);
-                    else finish4<DT_BF16, false, false>(p, gi, gj, v);
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, false, true>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, false, true>(p, gi, gj, v);
+                    else finish4<DT_BF16, false, false, true>(p, gi, gj, v);
                 }
             }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 }
