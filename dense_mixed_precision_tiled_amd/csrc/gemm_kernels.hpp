@@ -1148,54 +1148,68 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         // group (gi, gj..gj+3) inside M x N with vector-friendly C, D and bias
         auto gfull_at = [&](int gi) { return full || (p.cd_vec && p.splits == 1 && gi < p.M && gin); };
         // Linear part of the epilogue (alpha * sum + beta * C + bias, or sum + C)
-        // applied to the staged row block in place, with all its C and bias loads
-        // issued before any of its stores: on gfx9 a wait for a load also waits
-        // for every earlier store, so loading per group would serialise the
-        // stores.  (int32 outputs add C in 64 bits at the store instead.)
+        // applied in place to the staged groups that lie inside M x N (the
+        // vector groups), with all of a row block's C and bias loads issued
+        // before any of its stores: on gfx9 a wait for a load also waits for
+        // every earlier store, so loading per group would serialise the
+        // stores.  The loads are unconditional (a group outside M x N reads
+        // C(0, 0) and discards it), so no branch splits them.  Groups that
+        // cross the edge keep the whole epilogue for the finish step.  (int32
+        // outputs add C in 64 bits at the store instead.)
         auto linear = [&](auto out_tag, int i) {
             constexpr int OUT = decltype(out_tag)::value;
             f32x4 bcol = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.epi && p.bias && !p.bias_rows) {
-                if (p.cd_vec && gin) {
-                    bcol = *reinterpret_cast<const f32x4 *>(p.bias + gj);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (gj + e < p.N) bcol[e] = p.bias[gj + e];
-                }
-            }
+            if (p.epi && p.bias && !p.bias_rows && gin)
+                bcol = *reinterpret_cast<const f32x4 *>(p.bias + gj);
 #pragma nounroll
             for (int q0 = 0; q0 < PASSES; q0 += QB) {
-                f32x4 cv[QB];
+                // raw C bits (fp32: 4 words, 16-bit: 2), converted after all loads
+                u32x4 craw[QB];
                 float brow[QB];
-                Unroll<0, QB>::run([&](auto qq) {
-                    constexpr int q = decltype(qq)::value;
+                auto row_q = [&](int q) {
                     const int gi = row0 + i * MF + lane / LPR + (q0 + q) * RPP;
-                    cv[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    brow[q] = 0.0f;
-                    if (p.C) {
-                        if (gfull_at(gi)) {
-                            cv[q] = load_c4<OUT>(p, gi, gj);
-                        } else if (gi < p.M) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (gj + e < p.N) cv[q][e] = load_c(p, gi, gj + e);
+                    return gfull_at(gi) ? gi : -1;
+                };
+                if (p.C) {
+                    Unroll<0, QB>::run([&](auto qq) {
+                        constexpr int q = decltype(qq)::value;
+                        const int gi = row_q(q);
+                        const int64_t off = gi < 0 ? 0 : (int64_t)gi * p.ldc + gj;
+                        if constexpr (OUT == DT_F32) {
+                            craw[q] = *reinterpret_cast<const u32x4 *>(
+                                reinterpret_cast<const float *>(p.C) + off);
+                        } else {
+                            const u32x2 w = *reinterpret_cast<const u32x2 *>(
+                                reinterpret_cast<const uint16_t *>(p.C) + off);
+                            craw[q] = u32x4{w[0], w[1], 0u, 0u};
                         }
-                    }
-                    if (p.epi && p.bias && p.bias_rows && gi < p.M) brow[q] = p.bias[gi];
-                });
+                    });
+                }
+                if (p.epi && p.bias && p.bias_rows) {
+                    Unroll<0, QB>::run([&](auto qq) {
+                        constexpr int q = decltype(qq)::value;
+                        const int gi = row_q(q);
+                        brow[q] = p.bias[gi < 0 ? 0 : gi];
+                    });
+                }
                 Unroll<0, QB>::run([&](auto qq) {
                     constexpr int q = decltype(qq)::value;
-                    f32x4 *sp = reinterpret_cast<f32x4 *>(
-                        stage + (lane / LPR + (q0 + q) * RPP) * SROW + c4);
+                    const int rr = lane / LPR + (q0 + q) * RPP;
+                    if (!gfull_at(row0 + i * MF + rr)) return;
+                    f32x4 *sp = reinterpret_cast<f32x4 *>(stage + rr * SROW + c4);
                     f32x4 v = *sp;
+                    auto c = [&]() {
+                        if constexpr (OUT == DT_F32) return __builtin_bit_cast(f32x4, craw[q]);
+                        else return f32x4{from_out16<OUT>(lo16(craw[q][0])), from_out16<OUT>(hi16(craw[q][0])),
+                                          from_out16<OUT>(lo16(craw[q][1])), from_out16<OUT>(hi16(craw[q][1]))};
+                    };
                     if (p.epi) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) v[e] = p.alpha * v[e];
-                        if (p.C) v += p.beta * cv[q];
+                        if (p.C) v += p.beta * c();
                         if (p.bias) v += p.bias_rows ? f32x4{brow[q], brow[q], brow[q], brow[q]} : bcol;
-                    } else {
-                        v += cv[q];
+                    } else if (p.C) {
+                        v += c();
                     }
                     *sp = v;
                 });
@@ -1222,7 +1236,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
             // the compiler from moving the reads above the writes)
             __builtin_amdgcn_wave_barrier();
             if constexpr (IT != IT_I8) {
-                if (p.splits == 1 && (p.C || p.epi)) {
+                if (p.splits == 1 && p.cd_vec && (p.C || p.epi)) {
                     if (p.out_dtype == DT_F32) linear(std::integral_constant<int, DT_F32>{}, i);
                     else if (p.out_dtype == DT_F16) linear(std::integral_constant<int, DT_F16>{}, i);
                     else linear(std::integral_constant<int, DT_BF16>{}, i);
@@ -1245,18 +1259,18 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                         else if (p.out_dtype == DT_F16) finish4<DT_F16, true, true, true>(p, gi, gj, v);
                         else finish4<DT_BF16, true, true, true>(p, gi, gj, v);
                     } else {
-                        if (p.out_dtype == DT_F32) finish4<DT_F32, false, true, true>(p, gi, gj, v);
-                        else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true, true>(p, gi, gj, v);
-                        else finish4<DT_BF16, false, true, true>(p, gi, gj, v);
+                        if (p.out_dtype == DT_F32) finish4<DT_F32, false, true>(p, gi, gj, v);
+                        else if (p.out_dtype == DT_F16) finish4<DT_F16, false, true>(p, gi, gj, v);
+                        else finish4<DT_BF16, false, true>(p, gi, gj, v);
                     }
                 } else if (gfull) {
                     if (p.out_dtype == DT_F32) finish4<DT_F32, true, false, true>(p, gi, gj, v);
                     else if (p.out_dtype == DT_F16) finish4<DT_F16, true, false, true>(p, gi, gj, v);
                     else finish4<DT_BF16, true, false, true>(p, gi, gj, v);
                 } else {
-                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, false, true>(p, gi, gj, v);
-                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, false, true>(p, gi, gj, v);
-                    else finish4<DT_BF16, false, false, true>(p, gi, gj, v);
+                    if (p.out_dtype == DT_F32) finish4<DT_F32, false, false>(p, gi, gj, v);
+                    else if (p.out_dtype == DT_F16) finish4<DT_F16, false, false>(p, gi, gj, v);
+                    else finish4<DT_BF16, false, false>(p, gi, gj, v);
                 }
             }
             __builtin_amdgcn_wave_barrier();
