@@ -8,26 +8,26 @@ namespace libgemm {
 
 // Large square-ish problems: 256x256 block tile, 2x2 waves of 128x128
 // (4x4 MFMA 32x32x16 tiles per wave), BK 64, two LDS stages = 128 KiB.
-using CfgLarge = TileCfg<256, 256, 64, 2, 2, 32, 4>;
+using CfgLarge = TileCfg<256, 256, 64, 2, 2, 32>;
 // Large problems, eight waves: the same 256x256x64 tile over 2x4 waves of
 // 128x64 (4x2 MFMA tiles per wave), two waves per SIMD.  Each SIMD then
 // alternates between two instruction streams, which hides LDS latency
 // and issue gaps the single-wave schedule exposes.
-using CfgLarge8 = TileCfg<256, 256, 64, 2, 4, 32, 4>;
+using CfgLarge8 = TileCfg<256, 256, 64, 2, 4, 32>;
 // Mid-size problems: 128x128, 2x2 waves of 64x64.
-using CfgMedium = TileCfg<128, 128, 64, 2, 2, 32, 4>;
+using CfgMedium = TileCfg<128, 128, 64, 2, 2, 32>;
 // Small problems: 64x64, 2x2 waves of 32x32.
-using CfgSmall = TileCfg<64, 64, 64, 2, 2, 32, 4>;
+using CfgSmall = TileCfg<64, 64, 64, 2, 2, 32>;
 // Skinny M <= 16: 16x128x128 tile, 1x4 waves of 16x32 with the 16x16x32
 // MFMA, split-K so enough workgroups stream B.
-using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16, 1>;
+using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16>;
 
 // int8 entries: the same tiles in bytes (BK = 128 int8 values per LDS row of
 // 128 bytes), v_mfma_i32_32x32x32_i8 / v_mfma_i32_16x16x64_i8.
-using CfgLarge8I8 = TileCfg<256, 256, 128, 2, 4, 32, 4, 1>;
-using CfgMediumI8 = TileCfg<128, 128, 128, 2, 2, 32, 4, 1>;
-using CfgSmallI8 = TileCfg<64, 64, 128, 2, 2, 32, 4, 1>;
-using CfgSkinnyI8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 1>;
+using CfgLarge8I8 = TileCfg<256, 256, 128, 2, 4, 32, 1>;
+using CfgMediumI8 = TileCfg<128, 128, 128, 2, 2, 32, 1>;
+using CfgSmallI8 = TileCfg<64, 64, 128, 2, 2, 32, 1>;
+using CfgSkinnyI8 = TileCfg<16, 128, 256, 1, 4, 16, 1>;
 
 // OCP fp8 entries (E4M3 or E5M2 A and B): the same tiles in bytes, two
 // 16-byte chunks per lane and operand for v_mfma_scale_f32_32x32x64_f8f6f4 /
@@ -35,10 +35,10 @@ using CfgSkinnyI8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 1>;
 // fp8 tile uses four waves (one per SIMD, 128x128 each): with two waves per
 // SIMD the 32-byte fragments spill inside the K loop, and at 4096^3 the
 // four-wave tile is ~25% faster.
-using CfgLargeF8 = TileCfg<256, 256, 128, 2, 2, 32, 4, 1, 2>;
-using CfgMediumF8 = TileCfg<128, 128, 128, 2, 2, 32, 4, 1, 2>;
-using CfgSmallF8 = TileCfg<64, 64, 128, 2, 2, 32, 4, 1, 2>;
-using CfgSkinnyF8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 1, 2>;
+using CfgLargeF8 = TileCfg<256, 256, 128, 2, 2, 32, 1, 2>;
+using CfgMediumF8 = TileCfg<128, 128, 128, 2, 2, 32, 1, 2>;
+using CfgSmallF8 = TileCfg<64, 64, 128, 2, 2, 32, 1, 2>;
+using CfgSkinnyF8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 2>;
 
 typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
                                 dim3 grid, hipStream_t stream);

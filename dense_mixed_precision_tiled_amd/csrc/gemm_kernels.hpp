@@ -87,6 +87,7 @@ struct Params {
     int cd_vec;      // C, D rows allow 4-element vector access (aligned base, ld % 4 == 0)
     uint32_t a_bytes, b_bytes;  // vector path: A, B extents rounded up to 16 bytes
     int tiles_m, tiles_n;
+    int group_m;     // tile-rows per raster group (see map_tile)
     int splits;      // K slices (blockIdx.z); 1 = no split
     int k_per_split; // multiple of BK
     // extended epilogue: v = act(alpha * sum + beta * C + bias).  epi == 0 is
@@ -109,8 +110,7 @@ enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2 };
 // chunks of each operand one lane holds per MFMA: 1 for the 16-bit and int8
 // MFMAs, 2 for the fp8 ones.  In bytes, the tiles of every type share one
 // LDS layout.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MF_, int GROUP_M_,
-          int ES_ = 2, int FC_ = 1>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MF_, int ES_ = 2, int FC_ = 1>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -122,7 +122,6 @@ struct TileCfg {
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int TM = WTM / MF, TN = WTN / MF;
     static constexpr int CH = BK * ES / 16;  // 16-byte chunks per LDS row
-    static constexpr int GROUP_M = GROUP_M_;
     static_assert(MF == 32 || MF == 16, "MFMA shape");
     static_assert(ES == 1 || ES == 2, "element size");
     static_assert((BK * ES) % 128 == 0, "the LDS swizzle assumes rows of >= 128 bytes");
@@ -781,10 +780,10 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
 // ------------------------------------------------------------ tile mapping
 // Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
 // w % 8).  Renumber them so each XCD receives a contiguous range of tiles,
-// then walk tiles in groups of GROUP_M tile-rows, so the tiles that share
+// then walk tiles in groups of p.group_m tile-rows, so the tiles that share
 // A row-panels and B column-panels run on the same XCD's L2.
-template <int GROUP_M>
 __device__ __forceinline__ void map_tile(const Params &p, int w, int &tm, int &tn) {
+    const int GROUP_M = p.group_m;
     const int T = p.tiles_m * p.tiles_n;
     const int xcd = w & 7, local = w >> 3;
     const int per = T >> 3, rem = T & 7;
@@ -1050,7 +1049,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
 
     int tile_m, tile_n;
-    map_tile<CF::GROUP_M>(p, blockIdx.x, tile_m, tile_n);
+    map_tile(p, blockIdx.x, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
     const int kbeg = blockIdx.z * p.k_per_split;
