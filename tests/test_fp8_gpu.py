@@ -90,6 +90,24 @@ def test_fp8_with_the_extended_epilogue():
     assert np.array_equal(Dc.cpu().numpy().ravel(), ref)
 
 
+def test_multi_round_ragged_row_order_raster():
+    """17 x 19 tiles of 256 with K <= 2048 (plain row-order tile walk), E4M3,
+    ragged M and N: sampled outputs and whole edge rows."""
+    M, N, K = 4100, 4610, 1000
+    prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=FP8_E4M3,
+                          values="uniform", seed=9500)
+    log("case: fp8 %dx%dx%d" % (M, N, K))
+    dp = DeviceProblem(prob)
+    dp.run()
+    got = dp.result()
+    rows, cols = W.sample_indices(M, N, 4096, seed=9501)
+    er = np.repeat(np.array([0, 255, 256, 4095, 4096, 4099], np.int64), N)
+    ec = np.tile(np.arange(N, dtype=np.int64), 6)
+    rows, cols = np.concatenate([rows, er]), np.concatenate([cols, ec])
+    compare(prob, got[rows, cols], oracle_samples(prob, rows, cols), False, rows=rows,
+            cols=cols, label="fp8 multi-round sampled")
+
+
 @pytest.mark.parametrize("fmt", [FP8_E4M3, FP8_E5M2])
 def test_4096_fp8_sampled(fmt):
     n = 4096

@@ -116,6 +116,17 @@ def test_skinny_16x16384x16384(values, exact):
     _sampled_check(W.w_skinny(values), exact, seed=20304)
 
 
+@pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
+def test_multi_round_ragged_row_order_raster(values, exact):
+    """17 x 19 tiles of 256 (more than one per CU) with K <= 2048: the host
+    walks the tiles in plain row order instead of groups of 4 tile-rows.
+    Ragged M and N, fp32 C; sampled outputs plus whole rows at tile and
+    matrix edges."""
+    prob = W.make_problem(4100, 4610, 1000, values=values, c_values="normal" if values ==
+                          "uniform" else "int", seed=20311, name="4100x4610x1000 +C")
+    _sampled_check(prob, exact, seed=20312, extra_rows=[0, 255, 256, 2049, 4095, 4096, 4099])
+
+
 # ------------------------------------------------- every tile-table entry
 
 # tile-table entries: id -> block tile edge (None: the skinny split-K entry);
