@@ -107,6 +107,7 @@ WORKLOADS = {
 PEAK_I8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+W_F32, W_I8, W_I32, W_FP8_E4M3, W_FP8_E5M2 = 0, 3, 4, 5, 6  # gemm_dtype_t codes
 
 
 def make_workload(W, name):
@@ -133,11 +134,13 @@ def make_workload(W, name):
 
 def algorithmic_bytes(prob) -> int:
     """Compulsory HBM bytes: A and B once, C read once (if any), the bias once
-    (if any), D written once."""
-    osz = 4 if prob.out_dtype == 0 else 2
+    (if any), D written once, each at its element size (1 byte for int8 and
+    fp8 inputs, 2 for fp16/bf16; 4 for fp32 and int32 C/D, 2 for fp16/bf16)."""
+    isz = 1 if prob.in_dtype in (W_I8, W_FP8_E4M3, W_FP8_E5M2) else 2
+    osz = 4 if prob.out_dtype in (W_F32, W_I32) else 2
     c = prob.M * prob.N * osz if prob.C is not None else 0
     bias = 4 * prob.N if getattr(prob, "bias", None) is not None else 0
-    return 2 * prob.M * prob.K + 2 * prob.K * prob.N + c + bias + prob.M * prob.N * osz
+    return isz * (prob.M * prob.K + prob.K * prob.N) + c + bias + prob.M * prob.N * osz
 
 
 def main():
