@@ -46,20 +46,34 @@ def load_traffic():
 
 
 def cpu_baseline(prob, target_s: float):
-    """Time the oracle on the first R rows of D (all N columns, full K)."""
+    """Time the oracle on the first R rows of D (all N columns, full K): the
+    same computation as the workload (int8 through the integer oracle, the
+    extended epilogue through gemm_ex), into a host buffer of D's type."""
     import numpy as np
     import oracle
 
     oracle.build(force=False)
     threads = min(oracle.default_threads(), 16)
+    C = prob.D if prob.inplace else prob.C     # prob.D still holds the original C
+    layoutD = getattr(prob, "layoutD", 0)
+    dt = {W_F32: np.float32, W_I32: np.int32}.get(prob.out_dtype, np.uint16)
 
     def run_rows(R):
-        D = np.empty((R, prob.ldd), dtype=np.float32)
+        # A and B whole: with M = R the oracle reads rows < R of A in either layout
+        D = np.empty((R, prob.ldd) if layoutD == 0 else (prob.N, prob.ldd), dtype=dt)
+        args = (R, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA, prob.B.ravel(),
+                prob.ldb, prob.layoutB, None if C is None else C.ravel(), prob.ldc)
         t0 = time.perf_counter()
-        oracle.gemm(R, prob.N, prob.K, prob.A[:R].ravel(), prob.lda, prob.layoutA,
-                    prob.B.ravel(), prob.ldb, prob.layoutB, None, prob.ldc, D.ravel(),
-                    prob.ldd, prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf,
-                    nthreads=threads)
+        if prob.in_dtype == W_I8:
+            oracle.gemm_i8(*args, getattr(prob, "layoutC", 0), D.ravel(), prob.ldd, layoutD,
+                           prob.satf, nthreads=threads)
+        elif getattr(prob, "act", None) is not None:
+            oracle.gemm_ex(*args, prob.layoutC, D.ravel(), prob.ldd, layoutD, prob.in_dtype,
+                           prob.acc_dtype, prob.out_dtype, prob.satf, prob.alpha, prob.beta,
+                           prob.bias, prob.act, nthreads=threads)
+        else:
+            oracle.gemm(*args, D.ravel(), prob.ldd, prob.in_dtype, prob.acc_dtype,
+                        prob.out_dtype, prob.satf, nthreads=threads)
         return time.perf_counter() - t0
 
     probe_rows = threads
@@ -70,11 +84,12 @@ def cpu_baseline(prob, target_s: float):
     flops = 2.0 * rows * prob.N * prob.K
     return {
         "value": flops / t / 1e12,
-        "unit": "TFLOP/s",
+        "unit": "TOP/s" if prob.in_dtype == W_I8 else "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "first %d of %d rows of D (%d x %d outputs, K=%d), fp64 accumulate, "
-                  "%.1f s" % (rows, prob.M, rows, prob.N, prob.K, t),
+        "sample": "first %d of %d rows of D (%d x %d outputs, K=%d), %s, %.1f s"
+                  % (rows, prob.M, rows, prob.N, prob.K,
+                     "exact int64 sums" if prob.in_dtype == W_I8 else "fp64 accumulate", t),
     }
 
 

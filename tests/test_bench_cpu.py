@@ -60,3 +60,28 @@ def test_every_workload_has_a_description_and_bound():
         assert desc and bound in ("mfma", "hbm", "mfma_i8", "mfma_fp8"), name
         if gen is not None:
             assert callable(getattr(W, gen)), name
+
+
+@pytest.mark.parametrize("kind", ["f16_fp32", "f16_out", "i8", "fp8", "epilogue_colD", "inplace"])
+def test_cpu_baseline_runs_the_matching_oracle(kind):
+    """cpu_baseline times the oracle call that matches the workload's types and
+    epilogue (small shapes here)."""
+    if kind == "f16_fp32":
+        prob = W.make_problem(48, 40, 64, values="uniform", seed=11)
+    elif kind == "f16_out":
+        prob = W.make_problem(48, 40, 64, acc_dtype=W.F16, out_dtype=W.F16, values="uniform",
+                              c_values="normal", ldd=44, ldc=44, seed=12)
+    elif kind == "i8":
+        prob = W.make_int8_problem(48, 40, 64, values="full", c_values="int", seed=13)
+    elif kind == "fp8":
+        prob = W.make_problem(48, 40, 64, layoutB=W.COL_MAJOR, in_dtype=W.FP8_E4M3,
+                              values="uniform", seed=14)
+    elif kind == "epilogue_colD":
+        prob = W.make_epilogue_problem(48, 40, 64, layoutD=W.COL_MAJOR, values="uniform",
+                                       c_values="normal", bias_values="normal", act=2, seed=15)
+    else:
+        prob = W.make_problem(48, 40, 64, in_dtype=W.BF16, values="normal", c_values="normal",
+                              inplace=True, seed=16)
+    r = bench.cpu_baseline(prob, 0.02)
+    assert r["value"] > 0 and r["kind"] == "oracle" and r["cores"] >= 1
+    assert r["unit"] == ("TOP/s" if kind == "i8" else "TFLOP/s")
