@@ -93,6 +93,8 @@ def oracle_ex(ep, alpha=None, beta=None, bias="same", act=None, out_dtype=None, 
         ldd = D.shape[1]
     C = D if (ep.inplace and out_dtype is None and layoutD is None) else \
         (ep.D.copy() if ep.inplace else ep.C)
+    if (ep.beta if beta is None else beta) == 0:
+        C = None  # beta = 0 reads no C (and C's dtype need not match an overridden out_dtype)
     oracle.gemm_ex(ep.M, ep.N, ep.K, ep.A.ravel(), ep.lda, ep.layoutA, ep.B.ravel(), ep.ldb,
                    ep.layoutB, None if C is None else C.ravel(), ep.ldc, ep.layoutC,
                    D.ravel(), ldd, lD, ep.in_dtype, ep.acc_dtype if od == ep.out_dtype else F32,
@@ -188,6 +190,28 @@ def test_every_entry_relu_integer_exact(cid, out_dt, acc_dt, in_dt):
                                  values="int", c_values="int", bias_values="int",
                                  alpha=2.0, beta=-1.0, act=RELU, satf=1, seed=5100 + cid)
     _check(ep, True, cid, "cfg%d ReLU int out=%d" % (cid, out_dt))
+
+
+@pytest.mark.parametrize("cid", sorted(ENTRY_TILE))
+@pytest.mark.parametrize("out_dt,acc_dt", [(F32, F32), (F16, F16), (BF16, F32)])
+def test_every_entry_vector_epilogue_with_c_and_bias(cid, out_dt, acc_dt):
+    """alpha, beta * C, bias and an activation with row-major C and D whose
+    leading dimensions are multiples of 4 (vector C/D/bias access): the staged
+    pre-phase applies the linear part to the groups inside M x N, the groups
+    crossing column N take the element path.  Integer data, bit-exact; then
+    uniform data with GELU."""
+    M, N, K = _entry_shape(cid)
+    ld = (N + 3) // 4 * 4 + 4
+    ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
+                                 out_dtype=out_dt, acc_dtype=acc_dt, values="int",
+                                 c_values="int", bias_values="int", alpha=2.0, beta=-1.0,
+                                 act=RELU, ldc=ld, ldd=ld, seed=5300 + cid)
+    _check(ep, True, cid, "cfg%d vector epilogue int out=%d" % (cid, out_dt))
+    ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
+                                 out_dtype=out_dt, acc_dtype=acc_dt, values="uniform",
+                                 c_values="normal", bias_values="normal", alpha=0.75,
+                                 beta=-0.5, act=GELU, ldc=ld, ldd=ld, seed=5350 + cid)
+    _check(ep, False, cid, "cfg%d vector epilogue GELU out=%d" % (cid, out_dt))
 
 
 @pytest.mark.parametrize("layout", [ROW_MAJOR, COL_MAJOR])

@@ -194,6 +194,24 @@ def test_every_entry_output_modes(cid, M, N, K):
 
 
 @pytest.mark.parametrize("cid", sorted(ENTRY_TILE))
+@pytest.mark.parametrize("out_dt,acc_dt", [(F16, F16), (BF16, F32), (F32, F32)])
+def test_every_entry_c_on_the_vector_epilogue(cid, out_dt, acc_dt):
+    """Nonzero C with ldc = ldd a multiple of 4 (C and D vector-friendly):
+    interior tiles add C in the register epilogue, edge tiles in the staged
+    pre-phase (their groups crossing column N element by element).  Ragged M
+    and N (N % 4 = 3)."""
+    M, N, K = next((m, n, k) for c, m, n, k in _entry_shapes() if c == cid)
+    ld = (N + 3) // 4 * 4 + 4
+    for values, exact in (("int", True), ("uniform", False)):
+        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, in_dtype=F16,
+                              acc_dtype=acc_dt, out_dtype=out_dt, values=values,
+                              c_values="int" if exact else "normal", ldc=ld, ldd=ld,
+                              seed=2100 + cid)
+        _full_check(prob, exact, config=cid,
+                    label="cfg%d vector C out=%d %s" % (cid, out_dt, values))
+
+
+@pytest.mark.parametrize("cid", sorted(ENTRY_TILE))
 def test_unaligned_leading_dims(cid):
     # lda, ldb not multiples of 8 elements: the element-wise load path
     M, N, K = (37, 45, 77) if ENTRY_TILE[cid] is not None else (9, 300, 700)
