@@ -59,6 +59,21 @@ def test_fp8_output_modes(cid):
         _check(prob, False, cid, "fp8 cfg%d out=%d" % (cid, prob.out_dtype))
 
 
+
+@pytest.mark.parametrize("cid", sorted(F8_ENTRY_TILE))
+def test_fp8_vector_epilogue_with_c(cid):
+    """ldc = ldd a multiple of 4: nonzero C on the register epilogue
+    (interior tiles) and the staged path (edge tiles), fp32/fp16/bf16 out."""
+    M, N, K = _shape(cid)
+    ld = (N + 3) // 4 * 4 + 4
+    for out_dt in (F32, F16, BF16):
+        for values, exact in (("int", True), ("uniform", False)):
+            prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+                                  in_dtype=FP8_E4M3, out_dtype=out_dt, values=values,
+                                  c_values="int" if exact else "normal", ldc=ld, ldd=ld,
+                                  seed=9200 + cid + 10 * out_dt)
+            _check(prob, exact, cid, "fp8 cfg%d vector C out=%d %s" % (cid, out_dt, values))
+
 def test_fp8_unaligned_and_small_shapes():
     for shape in ((1, 1, 1), (17, 33, 65), (70, 45, 0), (100, 90, 300)):
         M, N, K = shape

@@ -71,6 +71,19 @@ def test_satf_clamps_and_in_place(cid):
     _check(prob, cid, "i8 cfg%d satf in place" % cid)
 
 
+@pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
+@pytest.mark.parametrize("satf", [0, 1])
+def test_vector_epilogue_with_c_near_the_int32_limits(cid, satf):
+    """ldc = ldd a multiple of 4 (vector C and D): interior tiles add C in
+    the register epilogue, edge tiles group by group; C spans the int32 range
+    so C + A x B wraps (satf = 0) or clamps (satf = 1) for some outputs."""
+    M, N, K = _shape(cid)
+    ld = (N + 3) // 4 * 4 + 4
+    prob = W.make_int8_problem(M, N, K, values="full", c_values="big", satf=satf, ldc=ld,
+                               ldd=ld, seed=8150 + cid + 10 * satf)
+    _check(prob, cid, "i8 cfg%d vector C satf %d" % (cid, satf))
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 1), (5, 7, 3), (33, 65, 129), (70, 45, 0),
                                    (64, 64, 4096 + 17)])
 def test_small_and_ragged_shapes(shape):
