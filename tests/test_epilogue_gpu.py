@@ -194,24 +194,27 @@ def test_every_entry_relu_integer_exact(cid, out_dt, acc_dt, in_dt):
 
 @pytest.mark.parametrize("cid", sorted(ENTRY_TILE))
 @pytest.mark.parametrize("out_dt,acc_dt", [(F32, F32), (F16, F16), (BF16, F32)])
-def test_every_entry_vector_epilogue_with_c_and_bias(cid, out_dt, acc_dt):
+@pytest.mark.parametrize("lcd", [ROW_MAJOR, COL_MAJOR])
+def test_every_entry_vector_epilogue_with_c_and_bias(cid, out_dt, acc_dt, lcd):
     """alpha, beta * C, bias and an activation with row-major C and D whose
     leading dimensions are multiples of 4 (vector C/D/bias access): the staged
     pre-phase applies the linear part to the groups inside M x N, the groups
     crossing column N take the element path.  Integer data, bit-exact; then
     uniform data with GELU."""
     M, N, K = _entry_shape(cid)
-    ld = (N + 3) // 4 * 4 + 4
-    ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
-                                 out_dtype=out_dt, acc_dtype=acc_dt, values="int",
+    # column-major C and D run as the transposed problem, with the bias per row
+    ld = (max(M, N) + 3) // 4 * 4 + 4
+    ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, layoutC=lcd,
+                                 layoutD=lcd, out_dtype=out_dt, acc_dtype=acc_dt, values="int",
                                  c_values="int", bias_values="int", alpha=2.0, beta=-1.0,
                                  act=RELU, ldc=ld, ldd=ld, seed=5300 + cid)
-    _check(ep, True, cid, "cfg%d vector epilogue int out=%d" % (cid, out_dt))
-    ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
-                                 out_dtype=out_dt, acc_dtype=acc_dt, values="uniform",
-                                 c_values="normal", bias_values="normal", alpha=0.75,
-                                 beta=-0.5, act=GELU, ldc=ld, ldd=ld, seed=5350 + cid)
-    _check(ep, False, cid, "cfg%d vector epilogue GELU out=%d" % (cid, out_dt))
+    _check(ep, True, cid, "cfg%d vector epilogue int out=%d CD%d" % (cid, out_dt, lcd))
+    ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, layoutC=lcd,
+                                 layoutD=lcd, out_dtype=out_dt, acc_dtype=acc_dt,
+                                 values="uniform", c_values="normal", bias_values="normal",
+                                 alpha=0.75, beta=-0.5, act=GELU, ldc=ld, ldd=ld,
+                                 seed=5350 + cid)
+    _check(ep, False, cid, "cfg%d vector epilogue GELU out=%d CD%d" % (cid, out_dt, lcd))
 
 
 @pytest.mark.parametrize("layout", [ROW_MAJOR, COL_MAJOR])
