@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import dense_mixed_precision_tiled_amd as lg
+import oracle
 from dense_mixed_precision_tiled_amd import workloads as W
 from dense_mixed_precision_tiled_amd.workloads import COL_MAJOR, F16, F32, ROW_MAJOR
 from gpu_util import DeviceProblem, compare, log, oracle_full, region
@@ -90,3 +91,39 @@ def test_autotune_rejects_in_place():
     dp = DeviceProblem(prob)
     st, cfg = lg.gemm_autotune(*_args(dp), None, 2, torch.cuda.current_stream().cuda_stream)
     assert st == -6 and cfg == -1
+
+
+@pytest.mark.parametrize("kind", ["i8", "fp8"])
+def test_autotune_8_bit_inputs_stays_in_its_class(kind):
+    """int8 and fp8 signatures only time the entries of their own class; the
+    recorded entry then runs for gemm_run, and D is bit-exact against the
+    oracle (integer-valued data)."""
+    lg.gemm_autotune_clear()
+    M, N, K = 700, 900, 512
+    if kind == "i8":
+        prob = W.make_int8_problem(M, N, K, values="full", c_values="int", seed=6300)
+        prefix = "i8_"
+    else:
+        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+                              in_dtype=W.FP8_E4M3, values="int", c_values="int", seed=6301)
+        prefix = "fp8_"
+    log("case: autotune %s %dx%dx%d" % (kind, M, N, K))
+    dp = DeviceProblem(prob)
+    s = torch.cuda.current_stream().cuda_stream
+    st, cfg = lg.gemm_autotune(*_args(dp), None, 2, s)
+    assert st == 0 and lg.gemm_config_name(cfg).startswith(prefix)
+    assert lg.gemm_autotune_lookup(M, N, K, prob.layoutA, prob.layoutB, prob.in_dtype,
+                                   prob.acc_dtype, prob.out_dtype) == cfg
+    got = dp.result()
+    if kind == "i8":
+        ref = prob.D.copy()
+        oracle.gemm_i8(M, N, K, prob.A.ravel(), prob.lda, prob.layoutA, prob.B.ravel(),
+                       prob.ldb, prob.layoutB, prob.C.ravel(), prob.ldc, ROW_MAJOR, ref.ravel(),
+                       prob.ldd, ROW_MAJOR, prob.satf)
+    else:
+        ref = oracle_full(prob)
+    assert np.array_equal(region(prob, got).view(np.uint8), region(prob, ref).view(np.uint8))
+    dp.reset_D()
+    dp.run()
+    assert np.array_equal(dp.result().view(np.uint8), got.view(np.uint8))
+    lg.gemm_autotune_clear()
