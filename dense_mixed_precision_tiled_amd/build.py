@@ -26,7 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wno-unused-command-line-argument"]
+         "-Wall", "-Wextra", "-Wno-unused-command-line-argument"]
 
 
 def sources():
@@ -39,6 +39,13 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, r.stdout, r.stderr))
+    # pass compiler warnings on (the host pass's note about the packed-fp32
+    # target feature, which it does not know, is expected)
+    warn = [ln for ln in r.stderr.splitlines()
+            if "warning" in ln and "packed-fp32" not in ln and "warning generated" not in ln
+            and "warnings generated" not in ln]
+    if warn:
+        print("\n".join(warn), file=sys.stderr)
     return obj
 
 

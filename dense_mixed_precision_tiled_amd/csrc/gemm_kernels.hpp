@@ -315,7 +315,7 @@ struct LoaderRC {
         return PARTIAL ? tid % NBLOCKS : j * THREADS + tid;
     }
 
-    __device__ __forceinline__ void init(int tid, int64_t ld, int r0, int R) {
+    __device__ __forceinline__ void init(int tid, int64_t /*ld: per load*/, int r0, int R) {
         const int rb = block(0, tid) % RCH;   // the same for every j
         const int col = min(r0 + rb * 8, (R - 1) & ~7);
         voff = (uint32_t)(col * 2);
