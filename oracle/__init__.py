@@ -24,7 +24,11 @@ arrays through ctypes.  Definitions followed (page title, section):
   column-major C and D (``gemm_ex``): "矩阵乘法优化可视化学习文档" section 6
   (epilogue fusion) and section 8 (bias/activation at the final store), and the
   accumulator layouts of "CUDA算子优化(5)：WMMA矩阵乘法" section "WMMA API解释"
-  items (3) and (4).
+  items (3) and (4);
+* the product form (``gemm_product``, ``gemm_i8_product``) of the same
+  definitions for whole outputs of large problems: the operands decoded
+  exactly to fp64, their product formed by numpy's fp64 matmul (a library
+  step), then the C epilogue, single rounding and satf above.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against values
 and properties the pages and the mathematics fix (no GPU involved).
@@ -117,6 +121,14 @@ def _load():
         lib.oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.oracle_round_f32_bits.restype = ctypes.c_uint32
         lib.oracle_round_f32_bits.argtypes = [ctypes.c_double]
+        lib.oracle_decode_array.restype = c_int
+        lib.oracle_decode_array.argtypes = [c_int, vp, i64, vp]
+        lib.oracle_finish_array.restype = c_int
+        lib.oracle_finish_array.argtypes = [i64, i64, vp, vp, i64, c_int, vp, i64, c_int,
+                                            c_int, c_int, dbl, dbl, fp, c_int, c_int]
+        lib.oracle_finish_i8_array.restype = c_int
+        lib.oracle_finish_i8_array.argtypes = [i64, i64, vp, vp, i64, c_int, vp, i64, c_int,
+                                               c_int]
         _lib = lib
     return _lib
 
@@ -337,3 +349,88 @@ def gemm_i8_sampled(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, 
     if rc != 0:
         raise ValueError("oracle_gemm_i8_sampled rejected its arguments")
     return out
+
+
+# ------------------------------------------------------------- product form
+
+def decode_array(X, dtype: int) -> np.ndarray:
+    """All elements of the flat array X (16-bit patterns, int8, fp8 bytes,
+    float32 or int32) decoded exactly to float64 by the C decoders."""
+    X = np.ascontiguousarray(X)
+    out = np.empty(X.size, dtype=np.float64)
+    if _load().oracle_decode_array(int(dtype), X.ctypes.data, X.size, out.ctypes.data) != 0:
+        raise ValueError("oracle_decode_array: unknown dtype %r" % dtype)
+    return out
+
+
+def _matrix(X, dtype, rows, cols, ld, layout) -> np.ndarray:
+    """The rows x cols matrix X(r, c) held in flat X (row-major: X[r*ld + c],
+    column-major: X[c*ld + r]), decoded to float64."""
+    outer, inner = (rows, cols) if layout == ROW_MAJOR else (cols, rows)
+    if rows == 0 or cols == 0:
+        return np.zeros((rows, cols))
+    flat = np.ascontiguousarray(X).ravel()
+    need = (outer - 1) * ld + inner
+    if flat.size < need or ld < inner:
+        raise ValueError("operand buffer too small for its shape and leading dimension")
+    v = decode_array(flat[:need], dtype)
+    v = np.concatenate([v, np.zeros(outer * ld - need)]).reshape(outer, ld)[:, :inner]
+    return v if layout == ROW_MAJOR else v.T
+
+
+def product_sums(M, N, K, A, lda, layoutA, B, ldb, layoutB, in_dtype) -> np.ndarray:
+    """S(i, j) = sum_k A(i, k) * B(k, j) in fp64 as an M x N dense array: the
+    exactly decoded operands multiplied by numpy's fp64 matmul.  Exact where
+    every partial sum is (integer-valued inputs); otherwise within fp64
+    rounding, about K * 2^-53 * sum_k |A(i,k) * B(k,j)|."""
+    if K == 0 or M == 0 or N == 0:
+        return np.zeros((M, N))
+    a = _matrix(A, in_dtype, M, K, lda, layoutA)
+    b = _matrix(B, in_dtype, K, N, ldb, layoutB)
+    return np.ascontiguousarray(a @ b)
+
+
+def gemm_product(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                 in_dtype, acc_dtype, out_dtype, satf, layoutC=ROW_MAJOR, layoutD=ROW_MAJOR,
+                 alpha=1.0, beta=1.0, bias=None, act=ACT_NONE, nthreads=None, sums=None):
+    """gemm / gemm_ex for whole outputs of large problems: the sums from
+    ``product_sums`` (or the given ``sums``), then the epilogue, one rounding
+    and satf of the C oracle.  Same arguments and results as ``gemm_ex``
+    (C == D in place; only D(i, j) with i < M, j < N written), up to the fp64
+    summation order (see product_sums); ``acc_dtype`` only names the call."""
+    del acc_dtype
+    _check_in(A)
+    _check_in(B)
+    _check_out(D, out_dtype)
+    if C is not None:
+        _check_out(C, out_dtype)
+    bias = _check_bias(bias, N)
+    S = product_sums(M, N, K, A, lda, layoutA, B, ldb, layoutB, in_dtype) if sums is None \
+        else np.ascontiguousarray(sums, dtype=np.float64)
+    nt = default_threads() if nthreads is None else nthreads
+    rc = _load().oracle_finish_array(M, N, _ptr(S), _ptr(C), ldc, layoutC, _ptr(D), ldd,
+                                     layoutD, out_dtype, int(bool(satf)), float(alpha),
+                                     float(beta), _ptr(bias), int(act), nt)
+    if rc != 0:
+        raise ValueError("oracle_finish_array rejected its arguments")
+    return D
+
+
+def gemm_i8_product(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, layoutC, D, ldd,
+                    layoutD, satf):
+    """gemm_i8 for whole outputs of large problems: the int8 operands as exact
+    fp64 values, their fp64 matmul (exact while K < 2^39, every partial sum
+    below 2^53), then + C and the wrap or clamp to int32 of the C oracle."""
+    _check_i8(A)
+    _check_i8(B)
+    _check_i32(D)
+    if C is not None:
+        _check_i32(C)
+    if K >= 2 ** 39:
+        raise ValueError("gemm_i8_product: fp64 sums are exact only for K < 2^39")
+    S = product_sums(M, N, K, A, lda, layoutA, B, ldb, layoutB, I8)
+    rc = _load().oracle_finish_i8_array(M, N, _ptr(S), _ptr(C), ldc, layoutC, _ptr(D), ldd,
+                                        layoutD, int(bool(satf)))
+    if rc != 0:
+        raise ValueError("oracle_finish_i8_array rejected its arguments")
+    return D

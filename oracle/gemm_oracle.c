@@ -499,6 +499,22 @@ typedef struct {
     int act;
 } job_ex_t;
 
+/*
+ * The epilogue of element (i,j) from its fp64 sum s, before the rounding:
+ * act(alpha * s + beta * C(i,j) + bias[j]); C is read only when present and
+ * beta != 0.
+ */
+static double epilogue_ex(double s, double alpha, double beta, const void *C, int out_dtype,
+                          int64_t c_off, const float *bias, int64_t j, int act)
+{
+    double v = alpha * s;
+    if (C && beta != 0.0)
+        v = v + beta * load_out(C, out_dtype, c_off);
+    if (bias)
+        v = v + (double)bias[j];
+    return apply_act(v, act);
+}
+
 /* One output element before the final rounding. */
 static double element_ex(const job_ex_t *g, int64_t i, int64_t j)
 {
@@ -510,12 +526,8 @@ static double element_ex(const job_ex_t *g, int64_t i, int64_t j)
         double prod = a * bb;
         s = s + prod;
     }
-    double v = g->alpha * s;
-    if (b->C && g->beta != 0.0)
-        v = v + g->beta * load_out(b->C, b->out_dtype, cd_offset(g->layoutC, b->ldc, i, j));
-    if (g->bias)
-        v = v + (double)g->bias[j];
-    return apply_act(v, g->act);
+    return epilogue_ex(s, g->alpha, g->beta, b->C, b->out_dtype,
+                       cd_offset(g->layoutC, b->ldc, i, j), g->bias, j, g->act);
 }
 
 /* Rows [begin, end): each row's values are computed before any is stored. */
@@ -815,5 +827,147 @@ int oracle_gemm_i8_sampled(int64_t M, int64_t N, int64_t K,
     g.satf = satf;
     g.rows = rows; g.cols = cols; g.out = out;
     run_split_i8(&g, nsamples, nthreads, sample_worker_i8);
+    return 0;
+}
+
+/* ============================================== product form (whole outputs)
+ *
+ * The same definitions for outputs too large for the per-element loops above:
+ * the caller forms the fp64 sums S(i,j) = sum_k A(i,k) * B(k,j) with a
+ * library fp64 matrix product of the exactly decoded operands (numpy's
+ * matmul, in oracle/__init__.py), and the functions below do the rest.  The
+ * library product sums in an order of its own, so S can differ from the
+ * k-ascending sum of the loops above by fp64 rounding (at most about
+ * K * 2^-53 * sum_k |A(i,k) * B(k,j)|); where every partial sum is exact in
+ * fp64 (integer-valued and other short dyadic inputs) the two agree bit for
+ * bit.  The epilogue, the single rounding and satf are the functions the
+ * loops use.
+ */
+
+/* n elements of dtype (an input type, F32 or I32) decoded exactly to fp64. */
+int oracle_decode_array(int dtype, const void *src, int64_t n, double *dst)
+{
+    if (n < 0)
+        return -1;
+    for (int64_t e = 0; e < n; ++e) {
+        switch (dtype) {
+        case ORACLE_F32: dst[e] = (double)((const float *)src)[e]; break;
+        case ORACLE_F16: dst[e] = oracle_decode_f16(((const uint16_t *)src)[e]); break;
+        case ORACLE_BF16: dst[e] = oracle_decode_bf16(((const uint16_t *)src)[e]); break;
+        case ORACLE_I8: dst[e] = (double)((const int8_t *)src)[e]; break;
+        case ORACLE_I32: dst[e] = (double)((const int32_t *)src)[e]; break;
+        case ORACLE_FP8_E4M3: dst[e] = oracle_decode_fp8_e4m3(((const uint8_t *)src)[e]); break;
+        case ORACLE_FP8_E5M2: dst[e] = oracle_decode_fp8_e5m2(((const uint8_t *)src)[e]); break;
+        default: return -1;
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    int64_t M, N;
+    const double *S;
+    const void *C; int64_t ldc; int layoutC;
+    void *D; int64_t ldd; int layoutD;
+    int out_dtype, satf;
+    double alpha, beta;
+    const float *bias;
+    int act;
+    int64_t begin, end;
+} job_fin_t;
+
+/* Rows [begin, end): each row's values are formed before any is stored. */
+static void *finish_worker(void *arg)
+{
+    const job_fin_t *g = (const job_fin_t *)arg;
+    double *row = (double *)malloc(sizeof(double) * (size_t)(g->N > 0 ? g->N : 1));
+    for (int64_t i = g->begin; i < g->end; ++i) {
+        for (int64_t j = 0; j < g->N; ++j)
+            row[j] = epilogue_ex(g->S[i * g->N + j], g->alpha, g->beta, g->C, g->out_dtype,
+                                 cd_offset(g->layoutC, g->ldc, i, j), g->bias, j, g->act);
+        for (int64_t j = 0; j < g->N; ++j)
+            store_out(g->D, g->out_dtype, cd_offset(g->layoutD, g->ldd, i, j),
+                      finish_element(row[j], g->out_dtype, g->satf));
+    }
+    free(row);
+    return NULL;
+}
+
+/*
+ * D(i,j) = satf(round(act(alpha * S(i,j) + beta * C(i,j) + bias[j]))) for
+ * i < M, j < N; S is M x N, row-major and dense.  alpha = beta = 1, no bias
+ * and no activation is the plain D = round(S + C) of oracle_gemm.  Nothing
+ * else of D is written; C == D (same layout and ld) is the in-place update.
+ */
+int oracle_finish_array(int64_t M, int64_t N, const double *S,
+                        const void *C, int64_t ldc, int layoutC,
+                        void *D, int64_t ldd, int layoutD,
+                        int out_dtype, int satf, double alpha, double beta,
+                        const float *bias, int act, int nthreads)
+{
+    if (M < 0 || N < 0 || act < ORACLE_ACT_NONE || act > ORACLE_ACT_GELU)
+        return -1;
+    if ((layoutC != ORACLE_ROW_MAJOR && layoutC != ORACLE_COL_MAJOR) ||
+        (layoutD != ORACLE_ROW_MAJOR && layoutD != ORACLE_COL_MAJOR))
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    job_fin_t g;
+    memset(&g, 0, sizeof g);
+    g.M = M; g.N = N; g.S = S;
+    g.C = C; g.ldc = ldc; g.layoutC = layoutC;
+    g.D = D; g.ldd = ldd; g.layoutD = layoutD;
+    g.out_dtype = out_dtype; g.satf = satf;
+    g.alpha = alpha; g.beta = beta; g.bias = bias; g.act = act;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    if (M < nthreads)
+        nthreads = (int)M;
+    pthread_t th[256];
+    job_fin_t jobs[256];
+    int started[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = g;
+        jobs[t].begin = M * t / nthreads;
+        jobs[t].end = M * (t + 1) / nthreads;
+        started[t] = (nthreads > 1) && pthread_create(&th[t], NULL, finish_worker, &jobs[t]) == 0;
+        if (!started[t])
+            finish_worker(&jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (started[t])
+            pthread_join(th[t], NULL);
+    return 0;
+}
+
+/*
+ * int8 -> int32 from the sums: D(i,j) = to_int32(S(i,j) + C(i,j)).  S holds
+ * the exact integer sums (the fp64 product of int8 values is exact while
+ * K < 2^39: every partial sum stays below 2^53); values that are not
+ * integers in that range are rejected (-1).
+ */
+int oracle_finish_i8_array(int64_t M, int64_t N, const double *S,
+                           const int32_t *C, int64_t ldc, int layoutC,
+                           int32_t *D, int64_t ldd, int layoutD, int satf)
+{
+    if (M < 0 || N < 0)
+        return -1;
+    if ((layoutC != ORACLE_ROW_MAJOR && layoutC != ORACLE_COL_MAJOR) ||
+        (layoutD != ORACLE_ROW_MAJOR && layoutD != ORACLE_COL_MAJOR))
+        return -1;
+    const double lim = 9007199254740992.0; /* 2^53 */
+    for (int64_t e = 0; e < M * N; ++e)
+        if (!(S[e] > -lim && S[e] < lim) || S[e] != floor(S[e]))
+            return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            int64_t v = (int64_t)S[i * N + j];
+            if (C)
+                v += C[cd_offset(layoutC, ldc, i, j)];
+            D[cd_offset(layoutD, ldd, i, j)] = to_int32(v, satf);
+        }
+    }
     return 0;
 }
