@@ -7,6 +7,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/libgemm.h"
 #include "gemm_configs.hpp"
@@ -86,7 +87,37 @@ bool is_fp8(int in_dtype) { return in_dtype == GEMM_FP8_E4M3 || in_dtype == GEMM
 int input_class(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : (is_fp8(in_dtype) ? 2 : 0); }
 int in_size(int in_dtype) { return (in_dtype == GEMM_I8 || is_fp8(in_dtype)) ? 1 : 2; }
 
-constexpr int kCUs = 256;  // MI355X compute units
+// Compute units and XCDs of the current device, read once per device from
+// its attributes (MI355X: 256 CUs in 8 XCDs, which is also the answer when no
+// device can be queried, e.g. for gemm_select_config on a host without GPU).
+struct Topology {
+    int cus, xcds;
+};
+constexpr int kMaxDevices = 64;
+constexpr Topology kDefaultTopology = {256, 8};
+std::mutex g_topo_mutex;
+Topology g_topo[kMaxDevices];
+bool g_topo_known[kMaxDevices];
+
+Topology topology() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return kDefaultTopology;
+    std::lock_guard<std::mutex> lock(g_topo_mutex);
+    if (!g_topo_known[dev]) {
+        Topology t = kDefaultTopology;
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            v > 0)
+            t.cus = v;
+        v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0)
+            t.xcds = v;
+        g_topo[dev] = t;
+        g_topo_known[dev] = true;
+    }
+    return g_topo[dev];
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -190,7 +221,7 @@ int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
     return GEMM_OK;
 }
 
-int select_config(int64_t M, int64_t N, int64_t K, int klass) {
+int select_config(int64_t M, int64_t N, int64_t K, int klass, int cus) {
     (void)K;
     // the same shape classes for every input class; entries per class
     static const int kByClass[3][4] = {
@@ -200,9 +231,9 @@ int select_config(int64_t M, int64_t N, int64_t K, int klass) {
     const int *e = kByClass[klass];
     if (M <= CfgSkinny::BM) return e[0];
     const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
-    if (t_large >= 3 * kCUs / 4) return e[1];
+    if (t_large >= 3 * cus / 4) return e[1];
     const int64_t t_medium = cdiv(M, CfgMedium::BM) * cdiv(N, CfgMedium::BN);
-    if (t_medium >= kCUs / 2) return e[2];
+    if (t_medium >= cus / 2) return e[2];
     return e[3];
 }
 
@@ -235,31 +266,32 @@ int tuned_config(const TuneKey &k) {
     return it == g_tune.end() ? -1 : it->second;
 }
 
-// Per (device, stream) split-K workspace, grown on demand, held until exit.
+// Split-K workspace, one per (device, stream), grown on demand with
+// hipMalloc.  g_ws_mutex is held by a call from the moment it takes the buffer
+// until both of its launches are enqueued, so the work of two calls on one
+// stream is enqueued one call after the other and each reads only its own
+// partial sums (stream order).  A buffer that is outgrown may still be in use
+// by work enqueued earlier, so it is never freed: it moves to g_ws_retired
+// and, like the current buffers, is kept until the process exits.
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, std::pair<float *, size_t>> g_ws;
+std::vector<float *> g_ws_retired;
 
-hipError_t workspace(hipStream_t stream, size_t bytes, float **out) {
+// The caller holds g_ws_mutex.
+hipError_t workspace_locked(hipStream_t stream, size_t bytes, float **out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto &slot = g_ws[std::make_pair(dev, stream)];
     if (slot.second < bytes) {
-        if (slot.first) {
-            // earlier work on this stream may still read the old buffer
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return e;
-            e = hipFree(slot.first);
-            if (e != hipSuccess) return e;
-            slot.first = nullptr;
-            slot.second = 0;
-        }
+        // grow at least 2x, so a sequence of growing calls retires few buffers
+        const size_t want = bytes > 2 * slot.second ? bytes : 2 * slot.second;
         void *ptr = nullptr;
-        e = hipMalloc(&ptr, bytes);
+        e = hipMalloc(&ptr, want);
         if (e != hipSuccess) return e;
+        if (slot.first) g_ws_retired.push_back(slot.first);
         slot.first = static_cast<float *>(ptr);
-        slot.second = bytes;
+        slot.second = want;
     }
     *out = slot.first;
     return hipSuccess;
@@ -299,12 +331,13 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
         layoutC = layoutC == GEMM_ROW_MAJOR ? GEMM_COL_MAJOR : GEMM_ROW_MAJOR;
         bias_rows = true;
     }
+    const Topology topo = topology();
     int id = config_id;
     if (id < 0) {
         const TuneKey key{M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
                           current_device()};
         id = tuned_config(key);
-        if (id < 0) id = select_config(M, N, K, klass);
+        if (id < 0) id = select_config(M, N, K, klass, topo.cus);
     }
     const Entry &E = kTable[id];
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
@@ -362,12 +395,13 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     // and plain row order is faster: its concurrent tiles write D in wider
     // column bands (16384^2 x 1024: 14% faster for fp16, 25% for int8 and
     // fp8; at 8192^3 row order was 5% slower, at 4096^3 and 6144^3 on par).
-    p.group_m = (E.BM == 256 && tiles > kCUs && K <= 2048) ? 1 : 4;
+    p.group_m = (E.BM == 256 && tiles > topo.cus && K <= 2048) ? 1 : 4;
+    p.xcds = topo.xcds;
 
     // K slices: enough workgroups for 4 per CU, each slice >= 8 K-tiles
     int splits = 1;
     if (E.split_k && K > 0) {
-        const int64_t want = cdiv(4 * kCUs, tiles);
+        const int64_t want = cdiv(4 * (int64_t)topo.cus, tiles);
         const int64_t most = cdiv(K, (int64_t)E.BK * 8);
         splits = (int)(want < most ? want : most);
         if (splits < 1) splits = 1;
@@ -377,27 +411,25 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     p.splits = splits;
     p.k_per_split = (int)kps;
 
-    if (splits > 1) {
-        float *ws = nullptr;
-        if (workspace(stream, (size_t)splits * (size_t)M * (size_t)N * sizeof(float), &ws) !=
-            hipSuccess)
-            return GEMM_ERR_HIP;
-        p.ws = ws;
-    }
     const int akc = layoutA == GEMM_ROW_MAJOR;
     const int bkc = layoutB == GEMM_COL_MAJOR;
     dim3 grid((unsigned)tiles, 1, (unsigned)splits);
     // the launcher's variant flag: bf16 among the 16-bit inputs, E5M2 among fp8
     const int variant = (in_dtype == GEMM_BF16 || in_dtype == GEMM_FP8_E5M2) ? 1 : 0;
-    if (E.launch(p, variant, akc, bkc, grid, stream) != hipSuccess)
+    if (splits == 1)
+        return E.launch(p, variant, akc, bkc, grid, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+
+    // split-K: slice kernel into the workspace, then the reduction into D
+    const size_t ws_bytes = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+    std::lock_guard<std::mutex> ws_lock(g_ws_mutex);
+    if (workspace_locked(stream, ws_bytes, &p.ws) != hipSuccess) return GEMM_ERR_HIP;
+    if (E.launch(p, variant, akc, bkc, grid, stream) != hipSuccess) return GEMM_ERR_HIP;
+    const int64_t total = M * N;
+    int64_t blocks = cdiv(total, 256);
+    if (blocks > 8 * (int64_t)topo.cus) blocks = 8 * (int64_t)topo.cus;
+    if (launch_params(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), p, stream) !=
+        hipSuccess)
         return GEMM_ERR_HIP;
-    if (splits > 1) {
-        const int64_t total = M * N;
-        int64_t blocks = cdiv(total, 256);
-        if (blocks > 8 * kCUs) blocks = 8 * kCUs;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
-    }
     return GEMM_OK;
 }
 
@@ -582,7 +614,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
                             nullptr, 1 + (layoutB == GEMM_ROW_MAJOR ? N : K), layoutB, nullptr,
                             1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr, 0);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
-    return select_config(M, N, K, input_class(in_dtype));
+    return select_config(M, N, K, input_class(in_dtype), topology().cus);
 }
 
 }  // extern "C"

@@ -83,6 +83,15 @@ LIBGEMM_DECLARE_LAUNCH_F8(small)
 LIBGEMM_DECLARE_LAUNCH_F8(skinny)
 #undef LIBGEMM_DECLARE_LAUNCH_F8
 
+// Launch a kernel taking Params by value; the launch's own status is returned
+// (not a sticky error left by an earlier call).
+template <class Kern>
+hipError_t launch_params(Kern kernel, dim3 grid, dim3 block, const Params &p, hipStream_t s) {
+    Params arg = p;
+    void *args[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, s);
+}
+
 template <class CF, int IT, bool AKC, bool BKC>
 hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
     // the K loop masks k >= kend only when some slice ends inside a K-tile
@@ -90,18 +99,15 @@ hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
     // int8 vector loads need both operands K-contiguous (the host's vec_ok
     // says so); other int8 layouts take the element-wise loads
     constexpr bool can_vec = CF::ES == 2 || (AKC && BKC);
+    const dim3 block(CF::THREADS);
     if (!can_vec || !p.vec_ok)
-        hipLaunchKernelGGL((gemm_mfma_kernel<CF, IT, AKC, BKC, false, false>), grid,
-                           dim3(CF::THREADS), 0, s, p);
-    else if constexpr (can_vec) {
+        return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, false, false>, grid, block, p, s);
+    if constexpr (can_vec) {
         if (ragged)
-            hipLaunchKernelGGL((gemm_mfma_kernel<CF, IT, AKC, BKC, true, true>), grid,
-                               dim3(CF::THREADS), 0, s, p);
-        else
-            hipLaunchKernelGGL((gemm_mfma_kernel<CF, IT, AKC, BKC, true, false>), grid,
-                               dim3(CF::THREADS), 0, s, p);
+            return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, true>, grid, block, p, s);
+        return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, false>, grid, block, p, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;  // not reached
 }
 
 template <class CF, int IT>

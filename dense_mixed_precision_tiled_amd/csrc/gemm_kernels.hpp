@@ -39,6 +39,8 @@
 
 #include <type_traits>
 
+#include "gemm_address.hpp"
+
 namespace libgemm {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -88,6 +90,7 @@ struct Params {
     uint32_t a_bytes, b_bytes;  // vector path: A, B extents rounded up to 16 bytes
     int tiles_m, tiles_n;
     int group_m;     // tile-rows per raster group (see map_tile)
+    int xcds;        // XCDs the device hands workgroups to (round-robin)
     int splits;      // K slices (blockIdx.z); 1 = no split
     int k_per_split; // multiple of BK
     // extended epilogue: v = act(alpha * sum + beta * C + bias).  epi == 0 is
@@ -163,11 +166,14 @@ __device__ __forceinline__ uint32_t pair_of(const u32x4 &a, const u32x4 &b, int 
 //
 // Vector path (16-byte aligned operands, extent < 4 GiB): 16-byte buffer
 // loads through a descriptor whose range is the operand's extent rounded up
-// to 16 bytes, so every read past the end returns zeros.  Per-lane offsets
-// are fixed for the K loop; the K position goes in the scalar offset.  Rows
-// beyond R are clamped to the last valid row (8-row chunk): they only feed
-// outputs that are never stored.  k >= kend must read as zero; with RAGGED
-// the loaded values are masked (only a ragged last K-tile has any such k).
+// to 16 bytes.  Rows beyond R are clamped to the last valid row (8-row
+// chunk): they only feed outputs that are never stored.  Per-lane offsets
+// are fixed for the K loop and the K position goes in the scalar offset,
+// except in RAGGED kernels (K not a multiple of BK): there the k position is
+// part of the per-lane offset and clamped to the chunk holding kend-1, and
+// the loaded values for k >= kend are masked to zero.  So every chunk read
+// holds an element of the matrix (gemm_address.hpp), whatever the range
+// check does with the scalar offset.
 // Threads beyond a small tile's chunk count duplicate a chunk (same value to
 // the same LDS address), which keeps the code free of branches.
 //
@@ -211,7 +217,7 @@ struct LoaderKC {
     static_assert(PARTIAL || TOTAL % THREADS == 0, "tile/threads");
     static_assert(PARTIAL || THREADS % CH == 0, "threads/chunks");
     u32x4 v[PER];
-    uint32_t voff[PER];  // byte offset of each chunk at k = 0
+    uint32_t voff[PER];  // byte offset of each chunk at k0 = 0 (row clamped)
     int kc;              // this thread's k offset inside the K-tile
 
     __device__ __forceinline__ static int chunk(int i, int tid) {
@@ -221,22 +227,34 @@ struct LoaderKC {
     __device__ __forceinline__ void init(int tid, int64_t ld, int r0, int R) {
         kc = (chunk(0, tid) % CH) * EPC;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int r = min(r0 + chunk(i, tid) / CH, R - 1);
-            voff[i] = (uint32_t)(((int64_t)r * ld + kc) * ES);
-        }
+        for (int i = 0; i < PER; ++i)
+            voff[i] = (uint32_t)kc_chunk_offset(r0 + chunk(i, tid) / CH, kc, R, 1, ld, ES, false);
     }
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t) {
+    // CLAMPK (kernels whose last K-tile is ragged): the k position goes into
+    // the per-lane offset, clamped to the chunk holding kend-1; otherwise it
+    // rides in the scalar offset (every k of every K-tile is < kend).
+    template <bool CLAMPK>
+    __device__ __forceinline__ u32x4 load_at(__amdgpu_buffer_rsrc_t rsrc, int i, int k0,
+                                             int kend) const {
+        if constexpr (CLAMPK)
+            return buf_load16(rsrc, voff[i] - (uint32_t)(kc * ES) +
+                                        (uint32_t)kc_k_offset(k0 + kc, kend, ES), 0u);
+        else
+            return buf_load16(rsrc, voff[i], (uint32_t)k0 * (uint32_t)ES);
+    }
+
+    template <bool CLAMPK>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t, int kend) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            v[i] = buf_load16(rsrc, voff[i], (uint32_t)k0 * (uint32_t)ES);
+        for (int i = 0; i < PER; ++i) v[i] = load_at<CLAMPK>(rsrc, i, k0, kend);
     }
 
     // the idx-th global load / LDS store of load() / store(), one instruction
-    template <int idx>
-    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t) {
-        v[idx] = buf_load16(rsrc, voff[idx], (uint32_t)k0 * (uint32_t)ES);
+    template <int idx, bool CLAMPK>
+    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t,
+                                             int kend) {
+        v[idx] = load_at<CLAMPK>(rsrc, idx, k0, kend);
     }
     template <int idx>
     __device__ __forceinline__ void store_one(u32x4 *lds, int tid) const {
@@ -317,27 +335,36 @@ struct LoaderRC {
 
     __device__ __forceinline__ void init(int tid, int64_t /*ld: per load*/, int r0, int R) {
         const int rb = block(0, tid) % RCH;   // the same for every j
-        const int col = min(r0 + rb * 8, (R - 1) & ~7);
-        voff = (uint32_t)(col * 2);
+        voff = (uint32_t)rc_chunk_offset(r0 + rb * 8, 0, R, 1, 0, false);
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) kg[j] = block(j, tid) / RCH;
     }
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld) {
+    // CLAMPK: the row k goes into the per-lane offset, clamped to kend-1;
+    // otherwise the K-tile's start rides in the scalar offset
+    template <bool CLAMPK>
+    __device__ __forceinline__ u32x4 load_at(__amdgpu_buffer_rsrc_t rsrc, int j, int kk, int k0,
+                                             int64_t ld, int kend) const {
         const uint32_t ldb = (uint32_t)ld * 2u;
+        if constexpr (CLAMPK)
+            return buf_load16(rsrc, voff + (uint32_t)imin(k0 + kg[j] * KB + kk, kend - 1) * ldb, 0u);
+        else
+            return buf_load16(rsrc, voff + (uint32_t)(kg[j] * KB + kk) * ldb, (uint32_t)k0 * ldb);
+    }
+
+    template <bool CLAMPK>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld, int kend) {
 #pragma unroll
         for (int j = 0; j < NBLK; ++j)
 #pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-                v[j][kk] = buf_load16(rsrc, voff + (uint32_t)(kg[j] * KB + kk) * ldb,
-                                      (uint32_t)k0 * ldb);
+            for (int kk = 0; kk < KB; ++kk) v[j][kk] = load_at<CLAMPK>(rsrc, j, kk, k0, ld, kend);
     }
 
-    template <int idx>
-    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld) {
+    template <int idx, bool CLAMPK>
+    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld,
+                                             int kend) {
         constexpr int j = idx / KB, kk = idx % KB;
-        const uint32_t ldb = (uint32_t)ld * 2u;
-        v[j][kk] = buf_load16(rsrc, voff + (uint32_t)(kg[j] * KB + kk) * ldb, (uint32_t)k0 * ldb);
+        v[j][kk] = load_at<CLAMPK>(rsrc, j, kk, k0, ld, kend);
     }
 
     __device__ __forceinline__ void mask(int k0, int kend) {
@@ -778,15 +805,17 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
 }
 
 // ------------------------------------------------------------ tile mapping
-// Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
-// w % 8).  Renumber them so each XCD receives a contiguous range of tiles,
-// then walk tiles in groups of p.group_m tile-rows, so the tiles that share
-// A row-panels and B column-panels run on the same XCD's L2.
+// Workgroups are handed to the device's p.xcds XCDs round-robin (workgroup w
+// runs on XCD w % xcds).  Renumber them so each XCD receives a contiguous
+// range of tiles (a bijection for any tile count), then walk tiles in groups
+// of p.group_m tile-rows, so the tiles that share A row-panels and B
+// column-panels run on the same XCD's L2.
 __device__ __forceinline__ void map_tile(const Params &p, int w, int &tm, int &tn) {
     const int GROUP_M = p.group_m;
     const int T = p.tiles_m * p.tiles_n;
-    const int xcd = w & 7, local = w >> 3;
-    const int per = T >> 3, rem = T & 7;
+    const int nx = p.xcds;
+    const int xcd = w % nx, local = w / nx;
+    const int per = T / nx, rem = T % nx;
     const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
     const int in_group = GROUP_M * p.tiles_n;
     const int g = t / in_group;
@@ -842,8 +871,8 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     auto gload = [&](int kt) {
         const int k0 = kbeg + kt * BK;
         if constexpr (VEC) {
-            la.load(ra, k0, p.lda);
-            lb.load(rb, k0, p.ldb);
+            la.template load<RAGGED>(ra, k0, p.lda, kend);
+            lb.template load<RAGGED>(rb, k0, p.ldb, kend);
             if constexpr (RAGGED) {  // only the prologue's stores use this directly
                 la.mask(k0, kend);
                 lb.mask(k0, kend);
@@ -917,9 +946,9 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     auto load_one = [&](int k0, auto g_tag) {
         constexpr int g = decltype(g_tag)::value;
         if constexpr (g < LA::NLOAD)
-            la.template load_one<g>(ra, k0, p.lda);
+            la.template load_one<g, RAGGED>(ra, k0, p.lda, kend);
         else
-            lb.template load_one<g - LA::NLOAD>(rb, k0, p.ldb);
+            lb.template load_one<g - LA::NLOAD, RAGGED>(rb, k0, p.ldb, kend);
     };
 
     // prologue: K-tile 0 in LDS[0], K-tile 1 in registers, step 0 fragments

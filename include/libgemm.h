@@ -34,8 +34,12 @@
  *  - satf is applied once, to the value rounded to out_dtype; MAX_NORM is the
  *    largest finite value of out_dtype.
  *  - Rounding to fp16 / bf16 is round-to-nearest-even.
- *  - Nothing outside rows [0,M) and columns [0,N) of D is written, and no
- *    element of A or B outside the M x K and K x N matrices is read.
+ *  - Nothing outside rows [0,M) and columns [0,N) of D is written.  A and B
+ *    are read in aligned 16-byte blocks (vector path) or element by element
+ *    (other alignments): every block read holds at least one element of the
+ *    M x K resp. K x N matrix, so bytes of the leading-dimension padding next
+ *    to those elements (and up to 15 bytes past the last element) may be
+ *    read, but never affect D; nothing else outside the matrices is read.
  *  - int8 (in_dtype GEMM_I8, acc and out GEMM_I32): the sum is exact; the
  *    result (+ C) wraps modulo 2^32, or with satf is clamped to the int32
  *    range.  satf needs K < 2^17, where the int32 accumulator cannot wrap.
@@ -107,15 +111,22 @@ typedef enum {
  *                on it; the call does not wait for it.
  *
  * Ownership: every pointer is owned by the caller and must stay valid until
- * the stream reaches the enqueued work.  The library keeps one internal
- * device workspace per device for split-K partial sums (allocated on first
- * need, grown on demand with hipMalloc, freed at unload); calls that overlap
- * on one device from different host threads are serialised around it.
+ * the stream reaches the enqueued work.  Problems split along K (M <= 16)
+ * use a device workspace the library owns for the partial sums: one per
+ * (device, stream) pair, allocated with hipMalloc on first need and grown
+ * on demand.  A call holds the workspace's lock from taking the buffer until
+ * both of its launches are enqueued, so calls from several host threads on
+ * one stream are enqueued one after the other; an outgrown buffer is never
+ * freed (work enqueued earlier may still use it).  Workspaces are kept until
+ * the process exits.
  *
  * Errors: argument errors are detected on the host before anything is
  * enqueued, and nothing is written.  GEMM_ERR_HIP reports a launch or
- * allocation failure; faults inside the kernels surface at the next
- * synchronisation of the stream.
+ * allocation failure (the launch's own status, not an earlier error); D is
+ * then not written, except that a split-K call whose reduction launch fails
+ * has already enqueued its slice kernel, which writes only the workspace.
+ * Faults inside the kernels surface at the next synchronisation of the
+ * stream.
  *
  * Speed: 16-byte vector loads are used where A and B base pointers are
  * 16-byte aligned and lda, ldb are multiples of 16 bytes (the pages' ldm

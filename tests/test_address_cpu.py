@@ -1,0 +1,26 @@
+"""The operand loads' address arithmetic, checked on the host: the kernels'
+loaders compose their byte offsets from the functions of
+``csrc/gemm_address.hpp``; ``address_check.cpp`` composes them the same way
+for every tile, thread, chunk and K-tile of a set of problems (the HGEMM
+workload's ragged K among them) and checks that every 16-byte chunk read lies
+inside the operand and holds one of its elements.  Built with g++ under
+AddressSanitizer and UndefinedBehaviorSanitizer."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "dense_mixed_precision_tiled_amd", "csrc")
+SRC = os.path.join(ROOT, "tests", "address_check.cpp")
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_every_chunk_read_lies_inside_the_operand(tmp_path):
+    exe = str(tmp_path / "address_check")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-I", CSRC, SRC, "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 failures" in r.stdout, r.stdout
