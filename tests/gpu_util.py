@@ -22,7 +22,7 @@ import torch
 
 import dense_mixed_precision_tiled_amd as lg
 import oracle
-from dense_mixed_precision_tiled_amd.workloads import (BF16, F16, F32, FP8_E4M3, FP8_E5M2,
+from dense_mixed_precision_tiled_amd.workloads import (BF16, F16, F32, FP8_E4M3, FP8_E5M2, I8,
                                                        SENTINEL_16, SENTINEL_F32, from_bits16)
 
 
@@ -93,6 +93,38 @@ def oracle_full(prob) -> np.ndarray:
                 None if C is None else C.ravel(), prob.ldc, D.ravel(), prob.ldd,
                 prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf)
     return D
+
+
+def oracle_whole(prob, sums=None) -> np.ndarray:
+    """The whole D buffer by the oracle's product form (fp64 library matmul of
+    the exactly decoded operands, then the C oracle's epilogue, rounding and
+    satf) -- the oracle for full outputs of the large workloads.  Works for
+    Problem (plain), EpilogueProblem (extended epilogue) and int8 problems;
+    padding keeps its sentinel.  ``sums``: precomputed product sums (reused
+    between calls that differ only in satf)."""
+    D = prob.D.copy()
+    C = D if prob.inplace else prob.C
+    Cf = None if C is None else C.ravel()
+    if prob.in_dtype == I8:
+        oracle.gemm_i8_product(prob.M, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                               prob.B.ravel(), prob.ldb, prob.layoutB, Cf, prob.ldc,
+                               getattr(prob, "layoutC", 0), D.ravel(), prob.ldd,
+                               getattr(prob, "layoutD", 0), prob.satf)
+        return D
+    ex = {}
+    if hasattr(prob, "act"):
+        ex = dict(layoutC=prob.layoutC, layoutD=prob.layoutD, alpha=prob.alpha, beta=prob.beta,
+                  bias=prob.bias, act=prob.act)
+    oracle.gemm_product(prob.M, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                        prob.B.ravel(), prob.ldb, prob.layoutB, Cf, prob.ldc, D.ravel(), prob.ldd,
+                        prob.in_dtype, prob.acc_dtype, prob.out_dtype, prob.satf, sums=sums, **ex)
+    return D
+
+
+def product_sums(prob) -> np.ndarray:
+    """sum_k A(i,k) B(k,j) in fp64 (M x N) by the oracle's product form."""
+    return oracle.product_sums(prob.M, prob.N, prob.K, prob.A.ravel(), prob.lda, prob.layoutA,
+                               prob.B.ravel(), prob.ldb, prob.layoutB, prob.in_dtype)
 
 
 def oracle_samples(prob, rows, cols) -> np.ndarray:
