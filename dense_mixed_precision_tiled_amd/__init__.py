@@ -23,7 +23,7 @@ __all__ = [
     "GEMM_ROW_MAJOR", "GEMM_COL_MAJOR", "GEMM_F32", "GEMM_F16", "GEMM_BF16", "GEMM_I8",
     "GEMM_I32", "GEMM_FP8_E4M3", "GEMM_FP8_E5M2",
     "GEMM_OK", "GemmError", "LIB_PATH", "library",
-    "gemm_run", "gemm_run_config", "gemm_validate", "gemm_status_string",
+    "gemm_run", "gemm_run_noalloc", "gemm_run_config", "gemm_validate", "gemm_status_string",
     "gemm_num_configs", "gemm_config_name", "gemm_select_config",
     "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU", "GemmEpilogue",
     "gemm_run_ex", "gemm_run_ex_config", "gemm_validate_ex",
@@ -39,6 +39,7 @@ STATUS_NAMES = {
     0: "GEMM_OK", -1: "GEMM_ERR_INVALID_DIM", -2: "GEMM_ERR_INVALID_LD",
     -3: "GEMM_ERR_NULL_PTR", -4: "GEMM_ERR_UNSUPPORTED", -5: "GEMM_ERR_INVALID_LAYOUT",
     -6: "GEMM_ERR_ALIASING", -7: "GEMM_ERR_HIP", -8: "GEMM_ERR_INVALID_CONFIG",
+    -9: "GEMM_ERR_SCRATCH_TOO_SMALL",
 }
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libgemm.so")
@@ -63,6 +64,7 @@ _GEMM_ARGS = [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _vp, _i64, _vp
               _int, _int, _int, _int, _vp]
 SIGNATURES = {
     "gemm_run": (_int, _GEMM_ARGS),
+    "gemm_run_noalloc": (_int, _GEMM_ARGS),
     "gemm_run_config": (_int, [_int] + _GEMM_ARGS),
     "gemm_validate": (_int, [_i64, _i64, _i64, _vp, _i64, _int, _vp, _i64, _int, _vp, _i64,
                              _vp, _i64, _int, _int, _int]),
@@ -113,6 +115,15 @@ def gemm_run(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
     """Enqueue D = A x B + C; returns the gemm_status_t code."""
     return library().gemm_run(M, N, K, A, lda, layoutA, B, ldb, layoutB, C or None, ldc,
                               D, ldd, in_dtype, acc_dtype, out_dtype, int(satf), stream or None)
+
+
+def gemm_run_noalloc(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,
+                     in_dtype, acc_dtype, out_dtype, satf, stream) -> int:
+    """gemm_run with no device allocation (split-K partial sums in the
+    library's fixed 32 MiB scratch); returns the status code."""
+    return library().gemm_run_noalloc(M, N, K, A, lda, layoutA, B, ldb, layoutB, C or None, ldc,
+                                      D, ldd, in_dtype, acc_dtype, out_dtype, int(satf),
+                                      stream or None)
 
 
 def gemm_run_config(config_id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd,

@@ -297,10 +297,41 @@ hipError_t workspace_locked(hipStream_t stream, size_t bytes, float **out) {
     return hipSuccess;
 }
 
+// Scratch of the allocation-free entry point (gemm_run_noalloc): split-K
+// partial sums in a device array of fixed size, one copy per device, held
+// until the process ends.  Host code never uses the array's name as an
+// address: on each device, the first gemm_run_noalloc call (with that device
+// current) looks up the array's device address with hipGetSymbolAddress and
+// keeps it; kernels get that address.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(float **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// Where run() takes the split-K workspace from.
+enum WorkspaceMode { WS_LIBRARY = 0, WS_STATIC_SCRATCH = 1 };
+
 int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
         int layoutA, const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
         void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
-        const gemm_epilogue_t *epi_arg, void *stream_handle) {
+        const gemm_epilogue_t *epi_arg, void *stream_handle, int ws_mode = WS_LIBRARY) {
     int st = validate(M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
                       acc_dtype, out_dtype, epi_arg, satf);
     if (st != GEMM_OK) return st;
@@ -421,8 +452,14 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
 
     // split-K: slice kernel into the workspace, then the reduction into D
     const size_t ws_bytes = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
-    std::lock_guard<std::mutex> ws_lock(g_ws_mutex);
-    if (workspace_locked(stream, ws_bytes, &p.ws) != hipSuccess) return GEMM_ERR_HIP;
+    std::unique_lock<std::mutex> ws_lock;
+    if (ws_mode == WS_STATIC_SCRATCH) {
+        if (ws_bytes > kScratchBytes) return GEMM_ERR_SCRATCH_TOO_SMALL;
+        if (scratch_address(&p.ws) != hipSuccess) return GEMM_ERR_HIP;
+    } else {
+        ws_lock = std::unique_lock<std::mutex>(g_ws_mutex);
+        if (workspace_locked(stream, ws_bytes, &p.ws) != hipSuccess) return GEMM_ERR_HIP;
+    }
     if (E.launch(p, variant, akc, bkc, grid, stream) != hipSuccess) return GEMM_ERR_HIP;
     const int64_t total = M * N;
     int64_t blocks = cdiv(total, 256);
@@ -576,6 +613,14 @@ int gemm_run(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
                out_dtype, satf, nullptr, stream);
 }
 
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
+                     const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, void *D,
+                     int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
+                     void *stream) {
+    return run(-1, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype, acc_dtype,
+               out_dtype, satf, nullptr, stream, WS_STATIC_SCRATCH);
+}
+
 int gemm_run_config(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
                     int layoutA, const void *B, int64_t ldb, int layoutB, const void *C,
                     int64_t ldc, void *D, int64_t ldd, int in_dtype, int acc_dtype,
@@ -596,6 +641,8 @@ const char *gemm_status_string(int status) {
     case GEMM_ERR_ALIASING: return "D overlaps A or B, or C partially overlaps D";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_INVALID_CONFIG: return "no such tile-table entry";
+    case GEMM_ERR_SCRATCH_TOO_SMALL:
+        return "split-K partial sums exceed the 32 MiB scratch of gemm_run_noalloc";
     default: return "unknown status";
     }
 }

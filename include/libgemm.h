@@ -80,8 +80,10 @@ typedef enum {
     GEMM_ERR_INVALID_LAYOUT = -5, /* layout not GEMM_ROW_MAJOR / GEMM_COL_MAJOR  */
     GEMM_ERR_ALIASING = -6,       /* D overlaps A or B, or C partially overlaps D */
     GEMM_ERR_HIP = -7,            /* the HIP runtime reported an error           */
-    GEMM_ERR_INVALID_CONFIG = -8  /* gemm_run_config: no such config, or the
+    GEMM_ERR_INVALID_CONFIG = -8, /* gemm_run_config: no such config, or the
                                      config cannot run this problem            */
+    GEMM_ERR_SCRATCH_TOO_SMALL = -9 /* gemm_run_noalloc: the split-K partial
+                                     sums need more than its fixed scratch     */
 } gemm_status_t;
 
 /*
@@ -149,6 +151,33 @@ int gemm_run(int64_t M, int64_t N, int64_t K,
              void *D, int64_t ldd,
              int in_dtype, int acc_dtype, int out_dtype,
              int satf, void *stream);
+
+/*
+ * gemm_run without any device allocation, for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, validation and results as gemm_run (the same
+ * kernels, bit-identical D).  Where gemm_run would take its split-K partial
+ * sums from a workspace it allocates (M <= 16), this call uses a scratch
+ * array of fixed size compiled into the library: 32 MiB of device memory per
+ * GPU the library runs on, held until the process ends.  Problems whose
+ * partial sums (splits * M * N * 4 bytes) exceed it return
+ * GEMM_ERR_SCRATCH_TOO_SMALL before anything is enqueued (on a 256-CU
+ * MI355X no problem needs more than about 17 MB).  Every call on a
+ * GPU shares that GPU's scratch, and nothing guards it: calls that can
+ * overlap on one GPU (other streams, other host threads) race on it and must
+ * be ordered by the caller.  The scratch needs no clearing (each call writes
+ * every partial sum it reads).  The call makes no hipMalloc, hipFree or other
+ * allocating call; its first call on a device looks up the scratch's device
+ * address (hipGetSymbolAddress), which allocates no memory of its own: the
+ * scratch is part of the library's device code object.
+ */
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, int layoutA,
+                     const void *B, int64_t ldb, int layoutB,
+                     const void *C, int64_t ldc,
+                     void *D, int64_t ldd,
+                     int in_dtype, int acc_dtype, int out_dtype,
+                     int satf, void *stream);
 
 /* Static text for a gemm_status_t value ("unknown status" otherwise). */
 const char *gemm_status_string(int status);

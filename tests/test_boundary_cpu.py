@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = lg.gemm_status_string(code)
         assert s and s != "unknown status", code
     assert lg.gemm_status_string(-99) == "unknown status"
