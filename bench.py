@@ -15,6 +15,12 @@ region starts.  Prints ONE JSON line:
                 first rows of D), on this host's cores
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+
+The ceilings the GEMM is read against are workloads too (lib/libgemm_measure.so):
+``--workload mfma_peak_32`` / ``mfma_peak_16`` (a stream of independent
+v_mfma_f32_32x32x16_f16 / 16x16x32_f16 on random fp16 operands in registers,
+one workgroup of four waves per CU) and ``--workload copy`` (a 16-byte
+load/store copy of 512 MiB).
 """
 from __future__ import annotations
 
@@ -53,7 +59,7 @@ def cpu_baseline(prob, target_s: float):
     import oracle
 
     oracle.build(force=False)
-    threads = min(oracle.default_threads(), 16)
+    threads = oracle.default_threads()   # every core this process may run on
     C = prob.D if prob.inplace else prob.C     # prob.D still holds the original C
     layoutD = getattr(prob, "layoutD", 0)
     dt = {W_F32: np.float32, W_I32: np.int32}.get(prob.out_dtype, np.uint16)
@@ -119,6 +125,17 @@ WORKLOADS = {
     "4096_fp8": (None, "M=N=K=4096 GEMM, fp8 E4M3 A row-major and B column-major "
                  "(uniform[-1,1] rounded to E4M3), fp32 accumulate and D, C=0", "mfma_fp8"),
 }
+# the measured ceilings (libgemm_measure): name -> (description, unit)
+MEASURE_WORKLOADS = {
+    "mfma_peak_32": ("MFMA stream: independent v_mfma_f32_32x32x16_f16 on random fp16 operands "
+                     "held in registers, 4 waves (one per SIMD) per CU, no memory traffic",
+                     "TFLOP/s"),
+    "mfma_peak_16": ("MFMA stream: independent v_mfma_f32_16x16x32_f16 on random fp16 operands "
+                     "held in registers, 4 waves (one per SIMD) per CU, no memory traffic",
+                     "TFLOP/s"),
+    "copy": ("device copy of 512 MiB with 16-byte loads and stores (read + write bytes)", "GB/s"),
+}
+MEASURE_LIB = os.path.join(ROOT, "dense_mixed_precision_tiled_amd", "lib", "libgemm_measure.so")
 PEAK_I8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
@@ -170,7 +187,11 @@ def main():
     ap.add_argument("--autotune", action="store_true",
                     help="run gemm_autotune on the workload first (untimed) and time the "
                          "entry it records")
-    ap.add_argument("--workload", default="4096_f16", choices=sorted(WORKLOADS),
+    ap.add_argument("--config", default=None,
+                    help="force this tile-table entry (by name) instead of the dispatcher's "
+                         "choice, for comparisons between entries")
+    ap.add_argument("--workload", default="4096_f16",
+                    choices=sorted(WORKLOADS) + sorted(MEASURE_WORKLOADS),
                     help="workload to time (default: the headline 4096^3 fp16->fp32)")
     args = ap.parse_args()
 
@@ -190,6 +211,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     lg.library()
+    if args.workload in MEASURE_WORKLOADS:
+        measure(args)
+        return
 
     prob, desc, bound = make_workload(W, args.workload)
     dev = torch.device("cuda:0")
@@ -222,6 +246,14 @@ def main():
         run = lg.gemm_run
     cfg = lg.gemm_select_config(prob.M, prob.N, prob.K, prob.layoutA, prob.layoutB,
                                 prob.in_dtype, prob.acc_dtype, prob.out_dtype)
+    if args.config is not None:
+        names = [lg.gemm_config_name(i) for i in range(lg.gemm_num_configs())]
+        if args.config not in names:
+            raise SystemExit("unknown --config %r; entries: %s" % (args.config, ", ".join(names)))
+        cfg = names.index(args.config)
+        forced = cfg
+        run = ((lambda *a: lg.gemm_run_ex_config(forced, *a)) if epi
+               else (lambda *a: lg.gemm_run_config(forced, *a)))
 
     tuned = None
     if args.autotune:
@@ -329,6 +361,92 @@ def main():
     }
     if not args.no_cpu_baseline and args.workload == "4096_f16":
         out["cpu_baseline"] = cpu_baseline(prob, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def measure(args):
+    """Time a ceiling workload of libgemm_measure with the same protocol (K
+    back-to-back steps for `value`, K more launches bracketed by HIP events
+    for the per-launch rate)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    if not os.path.exists(MEASURE_LIB):
+        raise RuntimeError("libgemm_measure.so is not built; run "
+                           "`python -m dense_mixed_precision_tiled_amd.build`")
+    lib = ctypes.CDLL(MEASURE_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.gemm_measure_mfma_stream.argtypes = [ctypes.c_int] * 4 + [vp, vp, vp]
+    lib.gemm_measure_mfma_flops.restype = i64
+    lib.gemm_measure_mfma_flops.argtypes = [ctypes.c_int] * 4
+    lib.gemm_measure_copy.argtypes = [vp, vp, i64, vp]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    desc, unit = MEASURE_WORKLOADS[args.workload]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if args.workload.startswith("mfma_peak"):
+        mf = int(args.workload.rsplit("_", 1)[1])
+        rng = np.random.default_rng(20260)
+        ops = (rng.random(32768, dtype=np.float32) * 2 - 1).astype(np.float16)   # 64 KiB
+        operands = torch.from_numpy(ops.view(np.int16)).to(dev)
+        blocks, threads, iters = cus, 256, 20000
+        out = torch.empty(blocks * threads, dtype=torch.float32, device=dev)
+        work = float(lib.gemm_measure_mfma_flops(mf, blocks, threads, iters))
+
+        def launch():
+            return lib.gemm_measure_mfma_stream(mf, blocks, threads, iters, operands.data_ptr(),
+                                                out.data_ptr(), stream.cuda_stream)
+        peak, bound, dtype = PEAK_TFLOPS, "mfma", "f16"
+        config = {"workload": desc, "mfma": "32x32x16" if mf == 32 else "16x16x32",
+                  "workgroups": blocks, "threads": threads, "rounds": iters}
+    else:
+        nbytes = 512 << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        work = 2.0 * nbytes
+
+        def launch():
+            return lib.gemm_measure_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                         stream.cuda_stream)
+        peak, bound, dtype = PEAK_HBM_GBS, "hbm", "u8"
+        config = {"workload": desc, "bytes_copied": nbytes}
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    for _ in range(args.warmup):
+        if launch() != 0:
+            raise RuntimeError("measurement launch failed")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if launch() != 0:
+            raise RuntimeError("measurement launch failed")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durations_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    mean_ms = sum(durations_ms) / len(durations_ms)
+    achieved = work / (mean_ms * 1e-3) / scale
+    out = {
+        "metric": "%s ceiling, workload %s" % ("MFMA" if bound == "mfma" else "HBM copy",
+                                               args.workload),
+        "value": round(work * args.steps / wall / scale, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": config,
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "launch_ms_mean": round(mean_ms, 5),
+                     "launch_ms_min": round(min(durations_ms), 5)},
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 

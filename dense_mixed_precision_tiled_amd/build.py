@@ -4,7 +4,8 @@
 
 Objects go to <repo>/_build/libgemm/, the library to
 dense_mixed_precision_tiled_amd/lib/libgemm.so (in-tree, so a snapshot of the
-tree carries it to the machine that runs it).
+tree carries it to the machine that runs it).  The measurement kernels
+(csrc/measure/, not part of libgemm) go to lib/libgemm_measure.so.
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libgemm.so")
+MEASURE_LIB = os.path.join(LIBDIR, "libgemm_measure.so")
+MEASURE_SRC = os.path.join(CSRC, "measure", "measure_kernels.hip")
 OBJDIR = os.path.join(ROOT, "_build", "libgemm")
 
 ARCH = "gfx950"
@@ -53,18 +56,25 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    jobs = jobs or min(len(srcs) + 1, max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        measure = ex.submit(_compile, MEASURE_SRC)
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        mobj = measure.result()
+    _link([mobj], MEASURE_LIB)
+    _link(objs, LIB)
+    if verbose:
+        print("built", LIB, "and", MEASURE_LIB)
+    return LIB
+
+
+def _link(objs, out: str):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
-    return LIB
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
