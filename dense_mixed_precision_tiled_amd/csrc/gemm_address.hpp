@@ -59,4 +59,59 @@ LIBGEMM_HD inline int64_t operand_range(int64_t outer, int64_t inner, int64_t ld
     return (((outer - 1) * ld + inner) * es + 15) & ~(int64_t)15;
 }
 
+// ------------------------------------------------------ LDS tile layouts
+// K-contiguous tile: row r holds the operand's k values of one row (M for
+// A, N for B) as 16-byte chunks; chunk c of row r sits at slot c ^ swz_kc(r).
+// Eight consecutive rows read at one chunk (the MFMA operand reads), and
+// eight rows 8 apart, land in eight different 16-byte bank groups.
+LIBGEMM_HD inline int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
+
+// R-contiguous tile (row-major B or column-major A kept as stored): k-row k
+// holds R values as R/8 chunks; chunk c of k-row k sits at slot
+// c ^ swz_rc(k, mf).  The transposed operand reads (ds_read_b64_tr_b16) of
+// one half-wave then touch distinct banks: with the 32x32 MFMA a half-wave
+// reads 4 k-rows x 64 bytes (the XOR moves whole 64-byte groups by k % 4),
+// with the 16x16 MFMA 8 k-rows x 32 bytes (32-byte groups by k % 4 and bit 3
+// of k).  Needs R >= 128 (16 chunks).
+LIBGEMM_HD inline int swz_rc(int k, int mf) {
+    return mf == 32 ? (k & 3) << 2 : ((k & 3) | ((k >> 1) & 4)) << 1;
+}
+
+// Direct global -> LDS loads write 16 bytes per lane to consecutive LDS
+// chunks (lane l of an instruction to chunk q0 + l).  The source a lane
+// reads is therefore the chunk that belongs at that slot:
+//   K-contiguous tile with ch chunks per row: LDS chunk q holds row
+//   q / ch, chunk (q % ch) ^ swz_kc(row), i.e. k = that chunk * (16 / es);
+//   R-contiguous tile with chr chunks per k-row: LDS chunk q holds k-row
+//   q / chr, rows 8 * ((q % chr) ^ swz_rc(k-row)) .. + 7.
+LIBGEMM_HD inline void dma_kc_source(int q, int ch, int &row, int &chunk) {
+    row = q / ch;
+    chunk = (q % ch) ^ swz_kc(row);
+}
+LIBGEMM_HD inline void dma_rc_source(int q, int chr, int mf, int &krow, int &chunk) {
+    krow = q / chr;
+    chunk = (q % chr) ^ swz_rc(krow, mf);
+}
+
+// Transposed operand read (ds_read_b64_tr_b16) from an R-contiguous tile with
+// rowbytes bytes per k-row: in each group of 16 lanes, lane L supplies the
+// address of 4 consecutive 16-bit values and lane j of the group receives
+// element j % 4 of lane 4f + (j % 16) / 4 as its element f (f = 0..3).  For
+// the MFMA operand of rows rb.. (32 or 16 of them, mf) at k step ks (16 or
+// 32 k values) and half h (k offset 0 or 4 inside the lane's 8), lane L
+// addresses k-row ks*kstep + kgrp + 4h + (L % 16) / 4 at row
+// rb + rsub + 4 * (L % 4), where for mf = 32 kgrp = 8 * (L / 32) and
+// rsub = 16 * ((L / 16) % 2), for mf = 16 kgrp = 8 * (L / 16) and rsub = 0.
+// Then lane j holds the rows' operand values X(rb + j % mf, k) for the 4
+// k-values k = ks*kstep + 8 * (j / mf) + 4h + 0..3 the MFMA expects.
+LIBGEMM_HD inline int tr_read_offset(int lane, int mf, int ks, int h, int rb, int rowbytes) {
+    const int g = lane / 16, f = (lane % 16) / 4, q = lane % 4;
+    const int kstep = mf == 32 ? 16 : 32;
+    const int kgrp = mf == 32 ? 8 * (g / 2) : 8 * g;
+    const int rsub = mf == 32 ? 16 * (g % 2) : 0;
+    const int krow = ks * kstep + kgrp + 4 * h + f;
+    const int row = rb + rsub + 4 * q;
+    return krow * rowbytes + (((row / 8) ^ swz_rc(krow, mf)) * 16) + (row % 8) * 2;
+}
+
 }  // namespace libgemm

@@ -11,8 +11,10 @@
 
 #include "../../include/libgemm.h"
 #include "gemm_configs.hpp"
+#include "gemm_validate.hpp"
 
 using namespace libgemm;
+using namespace libgemm_host;
 
 namespace libgemm {
 // Split-K reduction: D(i,j) = finish(sum over slices in slice order + C).
@@ -77,15 +79,23 @@ const Entry kTable[] = {
      2, launch_small_fp8},
     {"fp8_skinny_16x128x256_w1x4_mfma16x16x128_splitk", CfgSkinnyF8::BM, CfgSkinnyF8::BN,
      CfgSkinnyF8::BK, 1, 2, launch_skinny_fp8},
+    {"large_dma_256x256x64_w2x2_mfma32x32x16", CfgLargeDma::BM, CfgLargeDma::BN, CfgLargeDma::BK,
+     0, 0, launch_large_dma},
+    {"tiny_32x32x64_w1x1_mfma32x32x16", CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, 0, 0, launch_tiny},
+    {"large_dma_256x256x64_w2x2_mfma16x16x32", CfgLargeDma16::BM, CfgLargeDma16::BN,
+     CfgLargeDma16::BK, 0, 0, launch_large_dma16},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
 enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
        CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8,
-       CFG_F8_LARGE = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12 };
+       CFG_F8_LARGE = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12,
+       CFG_LARGE_DMA = 13, CFG_TINY = 14, CFG_LARGE_DMA16 = 15 };
 
-bool is_fp8(int in_dtype) { return in_dtype == GEMM_FP8_E4M3 || in_dtype == GEMM_FP8_E5M2; }
-int input_class(int in_dtype) { return in_dtype == GEMM_I8 ? 1 : (is_fp8(in_dtype) ? 2 : 0); }
-int in_size(int in_dtype) { return (in_dtype == GEMM_I8 || is_fp8(in_dtype)) ? 1 : 2; }
+// Entries whose kernels load operands straight into LDS: 16-byte aligned
+// operands only (vec_ok); others run the entry of the same tile shape
+// with register-staged loads.
+bool needs_vec(int id) { return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16; }
+
 
 // Compute units and XCDs of the current device, read once per device from
 // its attributes (MI355X: 256 CUs in 8 XCDs, which is also the answer when no
@@ -121,120 +131,35 @@ Topology topology() {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int out_size(int dt) { return (dt == GEMM_F32 || dt == GEMM_I32) ? 4 : 2; }
-
-// Byte range [lo, hi) of a matrix with `outer` lines of `inner` elements at
-// stride ld; empty when either count is zero.
-struct Range {
-    unsigned __int128 lo, hi;
-    bool empty() const { return hi <= lo; }
-};
-
-Range extent(const void *p, int64_t outer, int64_t inner, int64_t ld, int esize) {
-    Range r;
-    r.lo = (unsigned __int128)(uintptr_t)p;
-    if (outer <= 0 || inner <= 0) {
-        r.hi = r.lo;
-        return r;
-    }
-    r.hi = r.lo + ((unsigned __int128)(outer - 1) * (unsigned __int128)ld +
-                   (unsigned __int128)inner) * (unsigned __int128)esize;
-    return r;
-}
-
-bool overlap(const Range &a, const Range &b) {
-    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
-}
-
-const gemm_epilogue_t kPlainEpilogue = {1.0f, 1.0f, nullptr, GEMM_ACT_NONE, GEMM_ROW_MAJOR,
-                                         GEMM_ROW_MAJOR};
-
-int validate(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int layoutA,
-             const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc, const void *D,
-             int64_t ldd, int in_dtype, int acc_dtype, int out_dtype,
-             const gemm_epilogue_t *epi, int satf_arg) {
-    if (!epi) epi = &kPlainEpilogue;
-    const int64_t kMaxDim = 0x7fffffff;
-    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
-        return GEMM_ERR_INVALID_DIM;
-    if (in_dtype == GEMM_I8 && acc_dtype == GEMM_I32 && out_dtype == GEMM_I32 && satf_arg &&
-        K >= ((int64_t)1 << 17))
-        return GEMM_ERR_UNSUPPORTED;
-    auto layout_ok = [](int l) { return l == GEMM_ROW_MAJOR || l == GEMM_COL_MAJOR; };
-    if (!layout_ok(layoutA) || !layout_ok(layoutB) || !layout_ok(epi->layoutC) ||
-        !layout_ok(epi->layoutD))
-        return GEMM_ERR_INVALID_LAYOUT;
-    if (in_dtype != GEMM_F16 && in_dtype != GEMM_BF16 && in_dtype != GEMM_I8 && !is_fp8(in_dtype))
-        return GEMM_ERR_UNSUPPORTED;
-    if (in_dtype == GEMM_I8) {
-        // int8 x int8 -> int32: the plain epilogue only (C/D layouts allowed);
-        // satf clamps the exact sum, which the int32 accumulator holds only
-        // for K < 2^17 (|a*b| <= 2^14)
-        if (acc_dtype != GEMM_I32 || out_dtype != GEMM_I32) return GEMM_ERR_UNSUPPORTED;
-        if (epi->alpha != 1.0f || (C && epi->beta != 1.0f && epi->beta != 0.0f) || epi->bias ||
-            epi->activation != GEMM_ACT_NONE)
-            return GEMM_ERR_UNSUPPORTED;
-    } else if (acc_dtype == GEMM_F32) {
-        if (out_dtype != GEMM_F32 && out_dtype != GEMM_F16 && out_dtype != GEMM_BF16)
-            return GEMM_ERR_UNSUPPORTED;
-    } else if (acc_dtype == GEMM_F16) {
-        if (in_dtype != GEMM_F16 || out_dtype != GEMM_F16) return GEMM_ERR_UNSUPPORTED;
-    } else {
-        return GEMM_ERR_UNSUPPORTED;
-    }
-    if (epi->activation != GEMM_ACT_NONE && epi->activation != GEMM_ACT_RELU &&
-        epi->activation != GEMM_ACT_GELU)
-        return GEMM_ERR_UNSUPPORTED;
-    const int64_t a_inner = layoutA == GEMM_ROW_MAJOR ? K : M;
-    const int64_t a_outer = layoutA == GEMM_ROW_MAJOR ? M : K;
-    const int64_t b_inner = layoutB == GEMM_ROW_MAJOR ? N : K;
-    const int64_t b_outer = layoutB == GEMM_ROW_MAJOR ? K : N;
-    const int64_t c_inner = epi->layoutC == GEMM_ROW_MAJOR ? N : M;
-    const int64_t c_outer = epi->layoutC == GEMM_ROW_MAJOR ? M : N;
-    const int64_t d_inner = epi->layoutD == GEMM_ROW_MAJOR ? N : M;
-    const int64_t d_outer = epi->layoutD == GEMM_ROW_MAJOR ? M : N;
-    // C is read only when present and beta != 0
-    const bool reads_c = C && epi->beta != 0.0f;
-    // leading dimensions: at least one line's worth, and small enough that
-    // every element offset fits in 62 bits
-    const int64_t kMaxLd = (int64_t)1 << 40;
-    if (lda < 1 || lda < a_inner || lda > kMaxLd) return GEMM_ERR_INVALID_LD;
-    if (ldb < 1 || ldb < b_inner || ldb > kMaxLd) return GEMM_ERR_INVALID_LD;
-    if (ldd < 1 || ldd < d_inner || ldd > kMaxLd) return GEMM_ERR_INVALID_LD;
-    if (reads_c && (ldc < 1 || ldc < c_inner || ldc > kMaxLd)) return GEMM_ERR_INVALID_LD;
-    if (M == 0 || N == 0) return GEMM_OK;
-    if (!D) return GEMM_ERR_NULL_PTR;
-    if (K > 0 && (!A || !B)) return GEMM_ERR_NULL_PTR;
-
-    const int osz = out_size(out_dtype);
-    const Range rd = extent(D, d_outer, d_inner, ldd, osz);
-    const int isz = in_size(in_dtype);
-    const Range ra = K > 0 ? extent(A, a_outer, a_inner, lda, isz) : extent(A, 0, 0, 1, isz);
-    const Range rb = K > 0 ? extent(B, b_outer, b_inner, ldb, isz) : extent(B, 0, 0, 1, isz);
-    if (overlap(rd, ra) || overlap(rd, rb)) return GEMM_ERR_ALIASING;
-    if (epi->bias && overlap(extent(epi->bias, 1, N, N, 4), rd)) return GEMM_ERR_ALIASING;
-    if (reads_c) {
-        const bool in_place = (C == D) && (ldc == ldd) && (epi->layoutC == epi->layoutD);
-        if (!in_place && overlap(extent(C, c_outer, c_inner, ldc, osz), rd))
-            return GEMM_ERR_ALIASING;
-    }
-    return GEMM_OK;
-}
-
 int select_config(int64_t M, int64_t N, int64_t K, int klass, int cus) {
     (void)K;
     // the same shape classes for every input class; entries per class
-    static const int kByClass[3][4] = {
-        {CFG_SKINNY, CFG_LARGE8, CFG_MEDIUM, CFG_SMALL},
-        {CFG_I8_SKINNY, CFG_I8_LARGE8, CFG_I8_MEDIUM, CFG_I8_SMALL},
-        {CFG_F8_SKINNY, CFG_F8_LARGE, CFG_F8_MEDIUM, CFG_F8_SMALL}};
+    // (skinny, large, medium, small, tiny; the 8-bit classes have no tiny tile)
+    static const int kByClass[3][5] = {
+        {CFG_SKINNY, CFG_LARGE8, CFG_MEDIUM, CFG_SMALL, CFG_TINY},
+        {CFG_I8_SKINNY, CFG_I8_LARGE8, CFG_I8_MEDIUM, CFG_I8_SMALL, CFG_I8_SMALL},
+        {CFG_F8_SKINNY, CFG_F8_LARGE, CFG_F8_MEDIUM, CFG_F8_SMALL, CFG_F8_SMALL}};
     const int *e = kByClass[klass];
     if (M <= CfgSkinny::BM) return e[0];
     const int64_t t_large = cdiv(M, CfgLarge::BM) * cdiv(N, CfgLarge::BN);
     if (t_large >= 3 * cus / 4) return e[1];
     const int64_t t_medium = cdiv(M, CfgMedium::BM) * cdiv(N, CfgMedium::BN);
     if (t_medium >= cus / 2) return e[2];
-    return e[3];
+    const int64_t t_small = cdiv(M, CfgSmall::BM) * cdiv(N, CfgSmall::BN);
+    if (t_small >= cus / 2) return e[3];
+    return e[4];
+}
+
+// The dispatcher's large 16-bit tile: with both operands K-contiguous (A
+// row-major, B column-major) and 16-byte aligned, the LDS-DMA kernel with the
+// 16x16x32 MFMA (measured 6-8% faster at 4096^3: that MFMA sustains a higher
+// clock under the power limit); an N- or M-contiguous operand would need
+// transposed LDS reads, which cost more than the register-staged transpose
+// of the eight-wave tile.
+int refine_large(int id, bool aligned, int layoutA, int layoutB) {
+    if (id == CFG_LARGE8 && aligned && layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR)
+        return CFG_LARGE_DMA16;
+    return id;
 }
 
 // Autotuned choices: problem signature (as the kernels see it, after a
@@ -364,13 +289,16 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     }
     const Topology topo = topology();
     int id = config_id;
+    bool auto_choice = false;  // the static dispatcher's pick (not forced, not autotuned)
     if (id < 0) {
         const TuneKey key{M, N, K, layoutA, layoutB, in_dtype, acc_dtype, out_dtype,
                           current_device()};
         id = tuned_config(key);
-        if (id < 0) id = select_config(M, N, K, klass, topo.cus);
+        if (id < 0) {
+            id = select_config(M, N, K, klass, topo.cus);
+            auto_choice = true;
+        }
     }
-    const Entry &E = kTable[id];
     hipStream_t stream = static_cast<hipStream_t>(stream_handle);
 
     Params p{};
@@ -412,6 +340,14 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     // (the 8-bit vector loads need K-contiguous A and B: A row-major, B col-major)
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
+    if (needs_vec(id) && !p.vec_ok) {
+        // a forced entry that cannot run these operands is an error; the
+        // dispatcher's choice falls back to the register-staged large tile
+        if (config_id >= 0) return GEMM_ERR_INVALID_CONFIG;
+        id = CFG_LARGE8;
+    }
+    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB);
+    const Entry &E = kTable[id];
     const int osz = out_size(out_dtype);
     // register epilogue (vector C, D and bias access): aligned row-major C and D
     p.cd_vec = ((uintptr_t)D % (4 * osz) == 0) && (ldd % 4 == 0) &&
@@ -519,6 +455,11 @@ int autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int la
             if (hipEventRecord(ev[0], stream) != hipSuccess) { st = GEMM_ERR_HIP; break; }
             st = run(id, M, N, K, A, lda, layoutA, B, ldb, layoutB, C, ldc, D, ldd, in_dtype,
                      acc_dtype, out_dtype, satf, epi, stream_handle);
+            if (st == GEMM_ERR_INVALID_CONFIG) {  // this entry cannot run these operands
+                st = GEMM_OK;
+                cand = -1.0f;
+                break;
+            }
             if (st != GEMM_OK) break;
             float ms = 0.0f;
             if (hipEventRecord(ev[1], stream) != hipSuccess ||
@@ -661,7 +602,8 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
                             nullptr, 1 + (layoutB == GEMM_ROW_MAJOR ? N : K), layoutB, nullptr,
                             1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr, 0);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
-    return select_config(M, N, K, input_class(in_dtype), topology().cus);
+    return refine_large(select_config(M, N, K, input_class(in_dtype), topology().cus), true,
+                        layoutA, layoutB);
 }
 
 }  // extern "C"

@@ -18,9 +18,19 @@ using CfgLarge8 = TileCfg<256, 256, 64, 2, 4, 32>;
 using CfgMedium = TileCfg<128, 128, 64, 2, 2, 32>;
 // Small problems: 64x64, 2x2 waves of 32x32.
 using CfgSmall = TileCfg<64, 64, 64, 2, 2, 32>;
+// Tiny problems (fewer 64x64 tiles than half the CUs, e.g. 256^3): 32x32, one
+// wave, so the grid has four times as many workgroups.
+using CfgTiny = TileCfg<32, 32, 64, 1, 1, 32>;
 // Skinny M <= 16: 16x128x128 tile, 1x4 waves of 16x32 with the 16x16x32
 // MFMA, split-K so enough workgroups stream B.
 using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16>;
+// Large problems on the LDS-DMA K loop (gemm_dma_kernel): 256x256x64, 2x2
+// waves of 128x128 (one per SIMD; 4x4 MFMA 32x32x16 tiles, accumulators in
+// the AGPRs), operands loaded straight into LDS.  16-byte aligned operands
+// only.
+using CfgLargeDma = TileCfg<256, 256, 64, 2, 2, 32>;
+// The same with the 16x16x32 MFMA (8x8 tiles of 16x16 per wave).
+using CfgLargeDma16 = TileCfg<256, 256, 64, 2, 2, 16>;
 
 // int8 entries: the same tiles in bytes (BK = 128 int8 values per LDS row of
 // 128 bytes), v_mfma_i32_32x32x32_i8 / v_mfma_i32_16x16x64_i8.
@@ -57,6 +67,9 @@ LIBGEMM_DECLARE_LAUNCH(large8)
 LIBGEMM_DECLARE_LAUNCH(medium)
 LIBGEMM_DECLARE_LAUNCH(small)
 LIBGEMM_DECLARE_LAUNCH(skinny)
+LIBGEMM_DECLARE_LAUNCH(large_dma)
+LIBGEMM_DECLARE_LAUNCH(tiny)
+LIBGEMM_DECLARE_LAUNCH(large_dma16)
 #undef LIBGEMM_DECLARE_LAUNCH
 
 // one translation unit per int8 entry: kernels_<entry>_i8.hip (the bf flag of
@@ -108,6 +121,25 @@ hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
         return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, false>, grid, block, p, s);
     }
     return hipErrorInvalidValue;  // not reached
+}
+
+// LDS-DMA kernels: vector operands only (the host never sends others here).
+template <class CF, int IT, bool AKC, bool BKC>
+hipError_t launch_dma_one(const Params &p, dim3 grid, hipStream_t s) {
+    if (!p.vec_ok) return hipErrorInvalidValue;
+    const bool ragged = (p.K % CF::BK) != 0 || (p.k_per_split % CF::BK) != 0;
+    const dim3 block(CF::THREADS);
+    if (ragged) return launch_params(gemm_dma_kernel<CF, IT, AKC, BKC, true>, grid, block, p, s);
+    return launch_params(gemm_dma_kernel<CF, IT, AKC, BKC, false>, grid, block, p, s);
+}
+
+template <class CF, int IT>
+hipError_t launch_dma_layouts(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
+    if (akc)
+        return bkc ? launch_dma_one<CF, IT, true, true>(p, grid, s)
+                   : launch_dma_one<CF, IT, true, false>(p, grid, s);
+    return bkc ? launch_dma_one<CF, IT, false, true>(p, grid, s)
+               : launch_dma_one<CF, IT, false, false>(p, grid, s);
 }
 
 template <class CF, int IT>

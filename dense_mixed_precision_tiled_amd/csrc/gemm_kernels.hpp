@@ -137,7 +137,7 @@ struct TileCfg {
 // stored at position c ^ swz(r).  Eight consecutive rows read at one chunk,
 // and eight rows 8 apart written at one chunk, land in eight different
 // 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz(int r) { return swz_kc(r); }
 
 // ------------------------------------------------------------ small helpers
 __device__ __forceinline__ uint32_t lo16(uint32_t x) { return x & 0xffffu; }
@@ -147,14 +147,6 @@ __device__ __forceinline__ uint32_t hi16(uint32_t x) { return x >> 16; }
 __device__ __forceinline__ uint32_t half_of(const u32x4 &v, int e) {
     uint32_t d = v[e >> 1];
     return (e & 1) ? hi16(d) : lo16(d);
-}
-
-// {element e of a, element e of b} packed into one dword (low half from a),
-// for a and b holding 8 16-bit values each: one v_perm_b32 (byte select from
-// the pair {b, a}, a supplying bytes 0-3).
-__device__ __forceinline__ uint32_t pair_of(const u32x4 &a, const u32x4 &b, int e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], sel);
 }
 
 // ---------------------------------------------------------------- loaders
@@ -324,20 +316,31 @@ struct LoaderRC {
     static_assert(PERT % KB == 0, "blocks");
     static_assert(BK % KB == 0, "k groups");
     static_assert(PARTIAL || THREADS % RCH == 0, "threads/row chunks");
+    // Block b -> (8-row chunk rb, k-group kg).  PAIRS: two adjacent lanes
+    // take the same rb at two adjacent k-groups, and adjacent pairs adjacent
+    // 16 bytes of a k-row (the global loads stay coalesced).  Then one
+    // transposing store instruction of 32 lanes writes both 8-byte halves of
+    // the LDS chunks it touches, twice the banks of the plain mapping
+    // (rb = b % RCH), whose 32 lanes hit a quarter of the banks 4 deep.
+    static constexpr bool PAIRS =
+        (NBLOCKS % (2 * RCH) == 0) && (PARTIAL || THREADS % (2 * RCH) == 0);
     u32x4 v[NBLK][KB];  // v[j][kk]: 8 consecutive r at k = kg_j*KB + kk
     uint32_t voff;      // byte offset of this thread's 8-row chunk at k = 0
     int kg[NBLK];       // k-group of each block
 
-    // block b -> (kg, rb): rb fastest, so adjacent lanes read adjacent 16 B
     __device__ __forceinline__ static int block(int j, int tid) {
         return PARTIAL ? tid % NBLOCKS : j * THREADS + tid;
     }
+    __device__ __forceinline__ static int rb_of(int b) { return PAIRS ? (b >> 1) % RCH : b % RCH; }
+    __device__ __forceinline__ static int kg_of(int b) {
+        return PAIRS ? (b & 1) + 2 * (b / (2 * RCH)) : b / RCH;
+    }
 
     __device__ __forceinline__ void init(int tid, int64_t /*ld: per load*/, int r0, int R) {
-        const int rb = block(0, tid) % RCH;   // the same for every j
+        const int rb = rb_of(block(0, tid));   // the same for every j
         voff = (uint32_t)rc_chunk_offset(r0 + rb * 8, 0, R, 1, 0, false);
 #pragma unroll
-        for (int j = 0; j < NBLK; ++j) kg[j] = block(j, tid) / RCH;
+        for (int j = 0; j < NBLK; ++j) kg[j] = kg_of(block(j, tid));
     }
 
     // CLAMPK: the row k goes into the per-lane offset, clamped to kend-1;
@@ -381,7 +384,7 @@ struct LoaderRC {
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
             const int b = block(j, tid);
-            const int rb = b % RCH, kgb = b / RCH;
+            const int rb = rb_of(b), kgb = kg_of(b);
             const int gr = r0 + rb * 8;
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) {
@@ -403,10 +406,19 @@ struct LoaderRC {
         store_col(lds, tid, idx / 8, idx % 8);
     }
 
+    // {element e of a, element e of b} packed into one dword (low half from
+    // a): one v_perm_b32 (byte select from the pair {b, a}, a supplying bytes
+    // 0-3)
+    __device__ __forceinline__ static uint32_t pair_of(const u32x4 &a, const u32x4 &b, int e) {
+        return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+    }
+
+    // Transpose block j in registers: LDS row rb*8 + e receives the KB
+    // k-values of column e, at k offset kg*KB.
     __device__ __forceinline__ void store_col(u32x4 *lds, int tid, int j, int e) const {
         constexpr int CH = BK / 8;
         const int b = block(j, tid);
-        const int rb = b % RCH, kgb = b / RCH;
+        const int rb = rb_of(b), kgb = kg_of(b);
         const int kofs = kgb * KB;
         const int c = kofs / 8, sub = kofs % 8;  // chunk and element offset
         const int r = rb * 8 + e;
@@ -428,37 +440,11 @@ struct LoaderRC {
         }
     }
 
-    // Transpose each KB x 8 block in registers: LDS row (rb*8 + e) receives
-    // the KB k-values of column e, at k offset kg*KB.
     __device__ __forceinline__ void store(u32x4 *lds, int tid) const {
-        constexpr int CH = BK / 8;
 #pragma unroll
-        for (int j = 0; j < NBLK; ++j) {
-            const int b = block(j, tid);
-            const int rb = b % RCH, kgb = b / RCH;
-            const int kofs = kgb * KB;
-            const int c = kofs / 8, sub = kofs % 8;  // chunk and element offset
+        for (int j = 0; j < NBLK; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = rb * 8 + e;
-                u32x4 *dst = lds + r * CH + (c ^ swz(r));
-                if constexpr (KB == 8) {
-                    u32x4 w;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) w[q] = pair_of(v[j][2 * q], v[j][2 * q + 1], e);
-                    *dst = w;
-                } else if constexpr (KB == 4) {
-                    u32x2 w;
-                    w[0] = pair_of(v[j][0], v[j][1], e);
-                    w[1] = pair_of(v[j][2], v[j][3], e);
-                    reinterpret_cast<u32x2 *>(dst)[sub / 4] = w;
-                } else if constexpr (KB == 2) {
-                    reinterpret_cast<uint32_t *>(dst)[sub / 2] = pair_of(v[j][0], v[j][1], e);
-                } else {
-                    reinterpret_cast<uint16_t *>(dst)[sub] = (uint16_t)half_of(v[j][0], e);
-                }
-            }
-        }
+            for (int e = 0; e < 8; ++e) store_col(lds, tid, j, e);
     }
 };
 
@@ -1059,39 +1045,341 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     (void)store_slot;
 }
 
-// ------------------------------------------------------------------ kernel
-// VEC selects the vector (aligned) or the element-wise (unaligned) loads and
-// RAGGED whether the vector loads mask k >= kend; each combination is its own
-// kernel, with a single K loop to allocate registers for.
-template <class CF, int IT, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
-__global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
-    constexpr int BM = CF::BM, BN = CF::BN, CH = CF::CH;
+// ------------------------------------------------------ K loop, LDS DMA
+// The large tiles' K loop on gfx950's direct global -> LDS loads
+// (buffer_load_dwordx4 ... lds): no operand passes through registers on its
+// way to LDS, so there is no staging, no ds_write and no in-register
+// transpose.  Each operand keeps its storage order in LDS:
+//   K-contiguous (row-major A, column-major B): [rows][BK] in 16-byte chunks,
+//     read with ds_read_b128 (one chunk per lane and MFMA operand);
+//   R-contiguous (row-major B, column-major A): [BK][rows], read with the
+//     transposing ds_read_b64_tr_b16 (two per lane and MFMA operand).
+// The XOR swizzles (gemm_address.hpp) are applied on the global side: lane l
+// of a DMA instruction fills LDS chunk q0 + l, so it fetches the chunk that
+// belongs in that slot.
+//
+// Two LDS stages.  Iteration t computes K-tile t from stage t & 1; its last
+// MFMA step starts with: wait for this wave's DMA of tile t+1, barrier (every
+// wave's DMA of tile t+1 has landed and every wave has finished reading
+// stage t & 1), then the DMA of tile t+2 into stage t & 1 is issued across
+// that step's MFMAs, which also read tile t+1's first fragments.  So a
+// tile's loads have one full K-tile of MFMA work to land in.  In the last
+// two iterations there is no tile t+2: the same DMA instructions then load
+// the last tile again into a 1 KiB sink no one reads, which keeps the loop
+// body free of branches (a branch there made the compiler shuffle the
+// accumulators between register files).  The compiler does not order LDS
+// DMA against LDS reads; the explicit vmcnt wait and the barrier do.
+//
+// A ragged last K-tile (k >= kend inside it) is loaded with clamped
+// addresses, then its k >= kend part is zeroed in LDS before it is read.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7: no wait),
+    // lgkmcnt 11:8 (15: no wait)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LIBGEMM_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const char *p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LIBGEMM_LDS s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst, uint32_t voff,
+                                      uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LIBGEMM_LDS void *)lds_dst, 16, (int)voff,
+                                             (int)soff, 0, 0);
+}
+
+// One operand's DMA for the K loop: ROWS x BK tile of 16-bit values, KC or
+// R-contiguous storage, NWAVES waves sharing the tile's 1 KiB DMA blocks.
+template <int ROWS, int BK, int NWAVES, int MF, bool KC, bool CLAMPK>
+struct DmaOperand {
+    static constexpr int BYTES = ROWS * BK * 2;
+    static constexpr int NI = BYTES / 1024 / NWAVES;  // DMA instructions per wave
+    static_assert(BYTES % (1024 * NWAVES) == 0, "1 KiB DMA blocks per wave");
+    static constexpr int CH = BK / 8;      // KC: chunks per row
+    static constexpr int CHR = ROWS / 8;   // RC: chunks per k-row
+    static_assert(KC || ROWS >= 128, "the R-contiguous swizzle needs 16 chunks per k-row");
+    uint32_t voff[NI];  // byte offset at k0 = 0 (CLAMPK: without the k part)
+    int kpos[NI];       // CLAMPK: k position of the chunk (KC) or the k-row (RC)
+
+    __device__ __forceinline__ void init(int lane, int wave, int r0, int R, int64_t ld) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int q = (wave * NI + i) * 64 + lane;
+            int a, c;
+            if constexpr (KC) {
+                dma_kc_source(q, CH, a, c);  // a = row, chunk c holds k = 8c..8c+7
+                kpos[i] = 8 * c;
+                voff[i] = (uint32_t)kc_chunk_offset(r0 + a, CLAMPK ? 0 : 8 * c, R, 1, ld, 2, false);
+            } else {
+                dma_rc_source(q, CHR, MF, a, c);  // a = k-row, rows 8c..8c+7
+                kpos[i] = a;
+                voff[i] = (uint32_t)rc_chunk_offset(r0 + 8 * c, CLAMPK ? 0 : a, R, 1, ld, false);
+            }
+        }
+    }
+
+    // DMA instruction i of this wave for the K-tile at k0 into the stage at
+    // lds, or into the 1 KiB block sink when the stage is not to be written
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, char *lds, char *sink,
+                                          bool real, int wave, int i, int k0, int64_t ld,
+                                          int kend) const {
+        char *dst = real ? lds + (wave * NI + i) * 1024 : sink;
+        if constexpr (KC) {
+            if constexpr (CLAMPK)
+                dma16(rsrc, dst, voff[i] + (uint32_t)kc_k_offset(k0 + kpos[i], kend, 2), 0u);
+            else
+                dma16(rsrc, dst, voff[i], (uint32_t)k0 * 2u);
+        } else {
+            if constexpr (CLAMPK)
+                dma16(rsrc, dst, voff[i] + (uint32_t)imin(k0 + kpos[i], kend - 1) * (uint32_t)ld * 2u,
+                      0u);
+            else
+                dma16(rsrc, dst, voff[i], (uint32_t)k0 * (uint32_t)ld * 2u);
+        }
+    }
+
+    // zero k >= kvalid of the tile in LDS (the ragged last K-tile), threads
+    // tid of nthreads
+    __device__ __forceinline__ static void zero_tail(char *lds, int kvalid, int tid, int nthreads) {
+        if constexpr (KC) {
+            for (int q = tid; q < ROWS * CH; q += nthreads) {
+                const int r = q / CH, c = q % CH;  // logical chunk c: k = 8c..8c+7
+                const int keep = kvalid - 8 * c;
+                if (keep >= 8) continue;
+                u32x4 *dst = reinterpret_cast<u32x4 *>(lds + (r * CH + (c ^ swz_kc(r))) * 16);
+                *dst = keep <= 0 ? u32x4{0u, 0u, 0u, 0u} : keep_first(*dst, keep);
+            }
+        } else {
+            for (int q = tid; q < (BK - kvalid) * CHR; q += nthreads)
+                reinterpret_cast<u32x4 *>(lds + (kvalid + q / CHR) * ROWS * 2)[q % CHR] =
+                    u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+};
+
+template <class CF, int IT, bool A_KC, bool B_KC, bool RAGGED>
+__device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int kbeg, int kend,
+                                           typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
+                                           char *lds, int tid) {
+    constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK;
     constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
-    using Acc = typename AccT<MF>::type;
+    constexpr int NWAVES = CF::WAVES_M * CF::WAVES_N;
+    constexpr int KS = BK / CF::KSTEP;            // MFMA steps per K-tile
+    constexpr int KCH = CF::KSTEP * 2 / 16;       // 16-byte chunks per step (KC reads)
+    static_assert(CF::ES == 2 && CF::FC == 1, "16-bit operands");
+    static_assert(BK == 64, "LDS rows of 128 bytes (KC layout)");
+    using DA = DmaOperand<BM, BK, NWAVES, MF, A_KC, RAGGED>;
+    using DB = DmaOperand<BN, BK, NWAVES, MF, B_KC, RAGGED>;
+    constexpr int SA = DA::BYTES, SB = DB::BYTES;  // bytes per stage
+    char *const ldsA = lds, *const ldsB = lds + 2 * SA;
 
-    __shared__ u32x4 smem[2 * (BM + BN) * CH];
-    u32x4 *const sA = smem;                 // [2][BM*CH]
-    u32x4 *const sB = smem + 2 * BM * CH;   // [2][BN*CH]
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    if (nk <= 0) return;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+    DA da;
+    DB db;
+    da.init(lane, wave, m0, p.M, p.lda);
+    db.init(lane, wave, n0, p.N, p.ldb);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.B, (short)0, (int)p.b_bytes, 0x00020000);
+    char *const sink = lds + 2 * (SA + SB);  // 1 KiB that no one reads
+    // g-th DMA instruction of this wave for the tile at k0 into stage (real)
+    // or into the sink
+    auto dma_one = [&](int g, int stage, int k0, bool real) {
+        if (g < DA::NI) da.issue(ra, ldsA + stage * SA, sink, real, wave, g, k0, p.lda, kend);
+        else db.issue(rb, ldsB + stage * SB, sink, real, wave, g - DA::NI, k0, p.ldb, kend);
+    };
+    auto zero_ragged = [&](int stage, int k0) {  // the tile at k0 is the ragged last one
+        DA::zero_tail(ldsA + stage * SA, kend - k0, tid, CF::THREADS);
+        DB::zero_tail(ldsB + stage * SB, kend - k0, tid, CF::THREADS);
+    };
 
-    int tile_m, tile_n;
-    map_tile(p, blockIdx.x, tile_m, tile_n);
-    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    // per-lane LDS byte offsets of each fragment at step 0, stage 0
+    uint32_t a_off[TM], b_off[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int rb0 = wm * CF::WTM + i * MF;
+        if constexpr (A_KC) {
+            const int r = rb0 + (lane & (MF - 1));
+            a_off[i] = (uint32_t)(r * DA::CH + ((lane / MF) ^ swz_kc(r))) * 16u;
+        } else {
+            a_off[i] = (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BM * 2);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int rb0 = wn * CF::WTN + j * MF;
+        if constexpr (B_KC) {
+            const int r = rb0 + (lane & (MF - 1));
+            b_off[j] = (uint32_t)(r * DB::CH + ((lane / MF) ^ swz_kc(r))) * 16u;
+        } else {
+            b_off[j] = (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BN * 2);
+        }
+    }
 
-    const int kbeg = blockIdx.z * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
+    u32x4 fa[2][TM], fb[2][TN];
+    // fragment f (A fragments first, then B) of step ks from stage st into slot sl
+    auto read_one = [&](int st, auto ks_tag, auto sl_tag, auto f_tag) {
+        constexpr int ks = decltype(ks_tag)::value, sl = decltype(sl_tag)::value;
+        constexpr int f = decltype(f_tag)::value;
+        constexpr bool isA = f < TM;
+        constexpr bool kc = isA ? A_KC : B_KC;
+        constexpr int RB = isA ? BM * 2 : BN * 2;  // R-contiguous: bytes per k-row
+        const char *base;
+        uint32_t off;
+        if constexpr (isA) {
+            base = ldsA + st * SA;
+            off = a_off[f];
+        } else {
+            base = ldsB + st * SB;
+            off = b_off[f - TM];
+        }
+        u32x4 v;
+        if constexpr (kc) {
+            // K-contiguous: chunk ks*KCH + lane/MF of the row; the step's
+            // chunk bits and the lane's never overlap, so XOR adds them
+            v = *reinterpret_cast<const u32x4 *>(base + (off ^ (uint32_t)(ks * KCH * 16)));
+        } else {
+            // R-contiguous: the step and half move whole k-rows (k % 4 and
+            // bit 3 of k, which the swizzle uses, are the lane's own)
+            constexpr uint32_t kstep_rows = MF == 32 ? 16 : 32;
+            const u32x2 lo = ds_read_tr16(base + off + ks * kstep_rows * RB);
+            const u32x2 hi = ds_read_tr16(base + off + (ks * kstep_rows + 4) * RB);
+            v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+        if constexpr (isA) fa[sl][f] = v;
+        else fb[sl][f - TM] = v;
+    };
+    auto mfma_one = [&](auto sl_tag, auto m_tag) {
+        constexpr int sl = decltype(sl_tag)::value, m = decltype(m_tag)::value;
+        constexpr int i = m / TN, j = m % TN;
+        const u32x4(&xa)[1] = *reinterpret_cast<const u32x4(*)[1]>(&fa[sl][i]);
+        const u32x4(&xb)[1] = *reinterpret_cast<const u32x4(*)[1]>(&fb[sl][j]);
+        if constexpr (MF == 32) acc[i][j] = mfma32<IT, 1>(xb, xa, acc[i][j]);
+        else acc[i][j] = mfma16<IT, 1>(xb, xa, acc[i][j]);
+    };
 
-    Acc acc[TM][TN];
-    Unroll<0, TM>::run([&](auto ii) {
-        Unroll<0, TN>::run([&](auto jj) {
-            acc[decltype(ii)::value][decltype(jj)::value] = Acc{};
-        });
+    // prologue: tiles 0 and 1 in flight, wait for tile 0, its step-0 fragments
+    constexpr int NDMA = DA::NI + DB::NI;
+#pragma unroll
+    for (int g = 0; g < NDMA; ++g) dma_one(g, 0, kbeg, true);
+    if (nk > 1) {
+#pragma unroll
+        for (int g = 0; g < NDMA; ++g) dma_one(g, 1, kbeg + BK, true);
+        wait_vmcnt<NDMA>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if constexpr (RAGGED) {
+        if (kbeg + BK > kend) {
+            zero_ragged(0, kbeg);
+            __syncthreads();
+        }
+    }
+    Unroll<0, TM + TN>::run([&](auto f) {
+        read_one(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, f);
     });
 
-    k_loop<CF, IT, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
+    constexpr int NM = TM * TN, NR = TM + TN;
+    for (int t = 0; t < nk; ++t) {
+        const int cur = t & 1;
+        // the DMA of tile t+2; past the last tile the loads go to the sink
+        // (from the last tile's addresses), so the loop body has no branch
+        const bool more = t + 2 < nk;
+        const int k_pre = kbeg + min(t + 2, nk - 1) * BK;
+        Unroll<0, KS>::run([&](auto ks_tag) {
+            constexpr int ks = decltype(ks_tag)::value;
+            constexpr int sl = ks & 1;
+            if constexpr (ks == KS - 1) {
+                // tile t+1 has landed everywhere; stage cur is no longer read
+                wait_vmcnt<0>();
+                __syncthreads();
+                if constexpr (RAGGED) {
+                    if (t + 1 < nk && kbeg + (t + 2) * BK > kend) {
+                        zero_ragged(cur ^ 1, kbeg + (t + 1) * BK);
+                        __syncthreads();
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // one MFMA, then its share of the next step's fragment reads (in
+            // the order that step first uses them: A row 0, every B column,
+            // then the other A rows) and, in the last step, of the DMA of
+            // tile t+2
+            Unroll<0, NM>::run([&](auto m_tag) {
+                constexpr int m = decltype(m_tag)::value;
+                mfma_one(std::integral_constant<int, sl>{}, m_tag);
+                if constexpr (ks == KS - 1) {
+                    Unroll<0, NDMA>::run([&](auto g_tag) {
+                        constexpr int g = decltype(g_tag)::value;
+                        if constexpr (g * NM / NDMA == m) dma_one(g, cur, k_pre, more);
+                    });
+                }
+                auto read_next = [&](auto fq) {
+                    if constexpr (ks + 1 < KS)
+                        read_one(cur, std::integral_constant<int, ks + 1>{},
+                                 std::integral_constant<int, sl ^ 1>{}, fq);
+                    else
+                        read_one(cur ^ 1, std::integral_constant<int, 0>{},
+                                 std::integral_constant<int, sl ^ 1>{}, fq);
+                };
+                constexpr int r_lo = NR <= NM ? (m < NR ? m : NR) : m * NR / NM;
+                constexpr int r_hi = NR <= NM ? (m < NR ? m + 1 : NR) : (m + 1) * NR / NM;
+                Unroll<r_lo, r_hi>::run([&](auto q_tag) {
+                    constexpr int q = decltype(q_tag)::value;
+                    constexpr int fid = (q == 0) ? 0 : (q <= TN ? TM + q - 1 : q - TN);
+                    read_next(std::integral_constant<int, fid>{});
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    }
+}
+
+// ---------------------------------------------------------------- epilogue
+// Register group g (4 consecutive D columns) of one accumulator tile.  AGPR:
+// the accumulators live in the AGPRs (kernels with 256 of them per lane);
+// each group is then moved to VGPRs right where the epilogue uses it
+// (v_accvgpr_read, a register move), so the 256 accumulators are never all
+// needed in VGPRs at once.
+__device__ __forceinline__ float agpr_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+template <bool AGPR, class T>
+__device__ __forceinline__ f32x4 acc_group(const T &t, int g) {
+    if constexpr (AGPR)
+        return f32x4{agpr_read(t[4 * g]), agpr_read(t[4 * g + 1]), agpr_read(t[4 * g + 2]),
+                     agpr_read(t[4 * g + 3])};
+    else
+        return f32x4{t[4 * g], t[4 * g + 1], t[4 * g + 2], t[4 * g + 3]};
+}
+
+// Finish one BM x BN tile from its accumulators: each lane owns 4
+// consecutive columns of one row per register group.  smem (SMEM_BYTES of
+// LDS) is free for staging: the K loop's reads of it are complete.
+template <class CF, int IT, bool VEC, int SMEM_BYTES, bool AGPR = false>
+__device__ __forceinline__ void tile_epilogue(const Params &p,
+                                              typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
+                                              int m0, int n0, u32x4 *smem, int tid) {
+    constexpr int BM = CF::BM, BN = CF::BN;
+    constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
 
     // Epilogue.  Each lane owns 4 consecutive columns of one row per register
     // group.  Interior tiles with vector-friendly C/D and the plain epilogue
@@ -1137,8 +1425,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                 Unroll<0, NG>::run([&](auto gg) {
                     constexpr int g = decltype(gg)::value;
                     const int col = col_of(j, g);
-                    const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    const f32x4 v = acc_group<AGPR>(acc[i][j], g);
                     if constexpr (PRE) finish4<OUT, true, false, true>(p, row, col, v + cpre[j][g]);
                     else finish4<OUT, true, false>(p, row, col, v);
                 });
@@ -1167,7 +1454,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
         constexpr int PASSES = MF / RPP;       // passes per row block
         constexpr int QB = PASSES < 8 ? PASSES : 8;  // passes whose loads are in flight together
         static_assert(64 % LPR == 0 && PASSES % QB == 0, "lanes per staged row");
-        static_assert(CF::WAVES_M * CF::WAVES_N * MF * SROW * 4 <= (int)sizeof(smem),
+        static_assert(CF::WAVES_M * CF::WAVES_N * MF * SROW * 4 <= SMEM_BYTES,
                       "staging fits in the operand buffers");
         float *stage = reinterpret_cast<float *>(smem) + wave * MF * SROW;
         const int row0 = m0 + wm * CF::WTM, col0 = n0 + wn * WTN;
@@ -1255,8 +1542,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
                         constexpr int g = decltype(gg)::value;
                         *reinterpret_cast<f32x4 *>(stage + acc_row<MF>(lane) * SROW + j * MF +
                                                    acc_col<MF>(lane, g)) =
-                            f32x4{acc[ic][j][4 * g], acc[ic][j][4 * g + 1],
-                                  acc[ic][j][4 * g + 2], acc[ic][j][4 * g + 3]};
+                            acc_group<AGPR>(acc[ic][j], g);
                     });
                 });
             });
@@ -1304,6 +1590,68 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
             __builtin_amdgcn_wave_barrier();
         }
     }
+}
+
+// ------------------------------------------------------------------ kernel
+// VEC selects the vector (aligned) or the element-wise (unaligned) loads and
+// RAGGED whether the vector loads mask k >= kend; each combination is its own
+// kernel, with a single K loop to allocate registers for.
+template <class CF, int IT, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
+__global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
+    constexpr int BM = CF::BM, BN = CF::BN, CH = CF::CH;
+    constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
+    using Acc = typename AccT<MF>::type;
+
+    __shared__ u32x4 smem[2 * (BM + BN) * CH];
+    u32x4 *const sA = smem;                 // [2][BM*CH]
+    u32x4 *const sB = smem + 2 * BM * CH;   // [2][BN*CH]
+
+    const int tid = threadIdx.x;
+    int tile_m, tile_n;
+    map_tile(p, blockIdx.x, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+
+    Acc acc[TM][TN];
+    Unroll<0, TM>::run([&](auto ii) {
+        Unroll<0, TN>::run([&](auto jj) {
+            acc[decltype(ii)::value][decltype(jj)::value] = Acc{};
+        });
+    });
+
+    k_loop<CF, IT, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
+    tile_epilogue<CF, IT, VEC, (int)sizeof(smem)>(p, acc, m0, n0, smem, tid);
+}
+
+// Large tiles on the LDS-DMA K loop (16-bit operands with 16-byte aligned
+// rows; other operands take gemm_mfma_kernel's element-wise path).
+template <class CF, int IT, bool A_KC, bool B_KC, bool RAGGED>
+__global__ void __launch_bounds__(CF::THREADS) gemm_dma_kernel(Params p) {
+    constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK;
+    constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
+    using Acc = typename AccT<MF>::type;
+
+    // two stages of A and B, then the 1 KiB sink of the K loop's idle DMA
+    __shared__ u32x4 smem[2 * (BM + BN) * BK * 2 / 16 + 64];
+    const int tid = threadIdx.x;
+    int tile_m, tile_n;
+    map_tile(p, blockIdx.x, tile_m, tile_n);
+    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+
+    Acc acc[TM][TN];
+    Unroll<0, TM>::run([&](auto ii) {
+        Unroll<0, TN>::run([&](auto jj) {
+            acc[decltype(ii)::value][decltype(jj)::value] = Acc{};
+        });
+    });
+    dma_k_loop<CF, IT, A_KC, B_KC, RAGGED>(p, m0, n0, kbeg, kend, acc,
+                                           reinterpret_cast<char *>(smem), tid);
+    tile_epilogue<CF, IT, true, 2 * (BM + BN) * BK * 2, true>(p, acc, m0, n0, smem, tid);
+    wait_vmcnt<0>();  // the sink's loads land before the workgroup's LDS is released
 }
 
 }  // namespace libgemm

@@ -129,19 +129,25 @@ def _out_buffer(M: int, ld: int, out_dtype: int) -> np.ndarray:
     return np.full((M, ld), SENTINEL_16, dtype=np.uint16)
 
 
+def _round_up(n: int, a: int) -> int:
+    return (n + a - 1) // a * a
+
+
 def make_problem(M: int, N: int, K: int, *, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
                  in_dtype=F16, acc_dtype=F32, out_dtype=F32, satf=0,
                  values="uniform", c_values: Optional[str] = None, inplace=False,
                  lda=None, ldb=None, ldc=None, ldd=None, seed=1234,
-                 name="custom") -> Problem:
-    """Build a seeded problem.  c_values=None means C = NULL (C = 0)."""
+                 name="custom", align=1) -> Problem:
+    """Build a seeded problem.  c_values=None means C = NULL (C = 0).
+    Unset lda / ldb are the operand's line length rounded up to a multiple
+    of ``align`` elements (8: 16-byte lines for 16-bit inputs)."""
     rng_a = np.random.default_rng(seed)
     rng_b = np.random.default_rng(seed + 1)
     rng_c = np.random.default_rng(seed + 2)
     a_outer, a_inner = (M, K) if layoutA == ROW_MAJOR else (K, M)
     b_outer, b_inner = (K, N) if layoutB == ROW_MAJOR else (N, K)
-    lda = max(1, a_inner) if lda is None else lda
-    ldb = max(1, b_inner) if ldb is None else ldb
+    lda = _round_up(max(1, a_inner), align) if lda is None else lda
+    ldb = _round_up(max(1, b_inner), align) if ldb is None else ldb
     ldd = max(1, N) if ldd is None else ldd
     A = _operand(rng_a, a_outer, a_inner, lda, in_dtype, values)
     B = _operand(rng_b, b_outer, b_inner, ldb, in_dtype, values)
@@ -290,16 +296,17 @@ def make_epilogue_problem(M: int, N: int, K: int, *, layoutA=ROW_MAJOR, layoutB=
                           out_dtype=F32, satf=0, values="uniform",
                           c_values: Optional[str] = "normal", bias_values: Optional[str] = "normal",
                           alpha=1.0, beta=1.0, act=0, inplace=False, ldc=None, ldd=None,
-                          seed=4321, name="epilogue") -> EpilogueProblem:
+                          seed=4321, name="epilogue", align=1) -> EpilogueProblem:
     """Seeded inputs for the extended epilogue (same value recipes as
-    make_problem; the bias is drawn in fp32).  c_values=None: C = NULL."""
+    make_problem; the bias is drawn in fp32).  c_values=None: C = NULL.
+    lda / ldb: the line length rounded up to a multiple of ``align``."""
     rng_a = np.random.default_rng(seed)
     rng_b = np.random.default_rng(seed + 1)
     rng_c = np.random.default_rng(seed + 2)
     rng_bias = np.random.default_rng(seed + 5)
     a_outer, a_inner = (M, K) if layoutA == ROW_MAJOR else (K, M)
     b_outer, b_inner = (K, N) if layoutB == ROW_MAJOR else (N, K)
-    lda, ldb = max(1, a_inner), max(1, b_inner)
+    lda, ldb = _round_up(max(1, a_inner), align), _round_up(max(1, b_inner), align)
     A = _operand(rng_a, a_outer, a_inner, lda, in_dtype, values)
     B = _operand(rng_b, b_outer, b_inner, ldb, in_dtype, values)
     d_outer, d_inner = (M, N) if layoutD == ROW_MAJOR else (N, M)

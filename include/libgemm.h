@@ -190,8 +190,13 @@ const char *gemm_status_string(int status);
  *
  * gemm_num_configs: number of entries.
  * gemm_config_name: static text naming entry `config_id` (NULL if out of range).
- * gemm_select_config: the entry gemm_run would use for this problem, or a
- *                negative gemm_status_t if the arguments are invalid.
+ * gemm_select_config: the entry gemm_run would use for this problem with
+ *                16-byte aligned operand lines, or a negative gemm_status_t
+ *                if the arguments are invalid.  (Entries whose kernels load
+ *                operands straight into LDS take aligned operands only; for
+ *                others gemm_run runs the register-staged entry of the same
+ *                tile shape, and gemm_run_config with such an entry returns
+ *                GEMM_ERR_INVALID_CONFIG.)
  */
 int gemm_num_configs(void);
 const char *gemm_config_name(int config_id);

@@ -10,6 +10,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <initializer_list>
+
 #include "gemm_address.hpp"
 
 using namespace libgemm;
@@ -65,6 +67,25 @@ static void check_rc(int ROWS, int BK, int THREADS, int R, int K, int64_t ld, in
     const int PERT = partial ? 1 : TOTAL / THREADS;
     const int KB = PERT < 8 ? PERT : 8;
     const int NBLK = PERT / KB, NBLOCKS = TOTAL / KB;
+    // the loader's block -> (rb, kg) map: adjacent lanes pair up on one rb
+    const bool pairs = NBLOCKS % (2 * RCH) == 0 && (partial || THREADS % (2 * RCH) == 0);
+    auto rb_of = [&](int b) { return pairs ? (b >> 1) % RCH : b % RCH; };
+    auto kg_of = [&](int b) { return pairs ? (b & 1) + 2 * (b / (2 * RCH)) : b / RCH; };
+    {   // a bijection onto the tile's blocks, and rb the same for all of a thread's blocks
+        char *seen = (char *)calloc(NBLOCKS, 1);
+        for (int tid = 0; tid < THREADS; ++tid)
+            for (int j = 0; j < NBLK; ++j) {
+                const int b = partial ? tid % NBLOCKS : j * THREADS + tid;
+                const int b0 = partial ? tid % NBLOCKS : tid;
+                if (rb_of(b) != rb_of(b0)) fail("rc rb differs across blocks", tid, j, ROWS, BK);
+                const int id = kg_of(b) * RCH + rb_of(b);
+                if (id < 0 || id >= NBLOCKS) fail("rc block out of range", tid, j, id, NBLOCKS);
+                else seen[id] = 1;
+            }
+        for (int id = 0; id < NBLOCKS; ++id)
+            if (!seen[id]) fail("rc block not covered", id, ROWS, BK, THREADS);
+        free(seen);
+    }
     const int64_t range = operand_range(K, R, ld, 2);
     const int splits = (K + kps - 1) / kps;
     const bool ragged = (K % BK) != 0 || (kps % BK) != 0;
@@ -76,7 +97,7 @@ static void check_rc(int ROWS, int BK, int THREADS, int R, int K, int64_t ld, in
                     for (int j = 0; j < NBLK; ++j)
                         for (int kk = 0; kk < KB; ++kk) {
                             const int b = partial ? tid % NBLOCKS : j * THREADS + tid;
-                            const int rb = b % RCH, kg = b / RCH;
+                            const int rb = rb_of(b), kg = kg_of(b);
                             const int col = r0 + rb * 8;
                             const int64_t voff = rc_chunk_offset(col, 0, R, 1, 0, false);
                             const int k = k0 + kg * KB + kk;
@@ -92,6 +113,73 @@ static void check_rc(int ROWS, int BK, int THREADS, int R, int K, int64_t ld, in
                                 fail("rc wrong chunk", off, col, k, 0);
                         }
         }
+}
+
+// --------------------------------------------------------- LDS-DMA path
+// One operand tile of ROWS x BK 16-bit values through the DMA kernel's data
+// path, simulated: the value of X(r, k) is a unique code; the DMA mapping
+// (dma_kc_source / dma_rc_source) fills an LDS image chunk by chunk, then
+// every fragment read of every step is performed as the kernel does it --
+// ds_read_b128 at the KC offset, or two ds_read_b64_tr_b16 at
+// tr_read_offset with the instruction's lane exchange -- and each lane must
+// hold X(rb + lane % MF, k0 + 8 * (lane / MF) + e), e = 0..7, the MFMA's
+// operand layout.
+static uint16_t code(int r, int k) { return (uint16_t)(((r & 0x3ff) << 6) ^ (k * 40503u)); }
+
+static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves) {
+    const int bytes = ROWS * BK * 2, chunks = bytes / 16;
+    const int ni = bytes / 1024 / nwaves;
+    if (bytes % (1024 * nwaves)) { fail("dma blocks", ROWS, BK, nwaves, 0); return; }
+    uint16_t *lds = (uint16_t *)calloc(chunks * 8, 2);
+    int *filled = (int *)calloc(chunks, sizeof(int));
+    for (int w = 0; w < nwaves; ++w)
+        for (int i = 0; i < ni; ++i)
+            for (int l = 0; l < 64; ++l) {
+                const int q = (w * ni + i) * 64 + l;   // the LDS chunk lane l fills
+                int a, c;
+                if (KC) dma_kc_source(q, BK / 8, a, c); else dma_rc_source(q, ROWS / 8, MF, a, c);
+                for (int e = 0; e < 8; ++e)   // KC: row a, k = 8c+e; RC: k-row a, row 8c+e
+                    lds[q * 8 + e] = KC ? code(a, 8 * c + e) : code(8 * c + e, a);
+                filled[q]++;
+            }
+    for (int q = 0; q < chunks; ++q)
+        if (filled[q] != 1) fail("dma chunk filled times", q, filled[q], ROWS, KC);
+    const int kstep = MF == 32 ? 16 : 32;
+    for (int ks = 0; ks < BK / kstep; ++ks)
+        for (int rb = 0; rb < ROWS; rb += MF) {
+            uint16_t got[64][8];
+            if (KC) {
+                const int kch = kstep * 2 / 16;
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int r = rb + lane % MF;
+                    const uint32_t off = (uint32_t)(r * (BK / 8) + ((lane / MF) ^ swz_kc(r))) * 16u;
+                    const uint32_t a = off ^ (uint32_t)(ks * kch * 16);
+                    for (int e = 0; e < 8; ++e) got[lane][e] = lds[a / 2 + e];
+                }
+            } else {
+                for (int h = 0; h < 2; ++h) {
+                    uint16_t in[64][4];
+                    for (int L = 0; L < 64; ++L) {
+                        const int off = tr_read_offset(L, MF, ks, h, rb, ROWS * 2);
+                        if (off % 8 || off < 0 || off + 8 > bytes) fail("tr offset", off, L, ks, h);
+                        for (int e = 0; e < 4; ++e) in[L][e] = lds[off / 2 + e];
+                    }
+                    // the instruction's exchange: lane j element f <- lane
+                    // 16*(j/16) + 4f + (j%16)/4, element j%4
+                    for (int j = 0; j < 64; ++j)
+                        for (int f = 0; f < 4; ++f)
+                            got[j][4 * h + f] = in[16 * (j / 16) + 4 * f + (j % 16) / 4][j % 4];
+                }
+            }
+            for (int lane = 0; lane < 64; ++lane)
+                for (int e = 0; e < 8; ++e) {
+                    const int r = rb + lane % MF, k = ks * kstep + 8 * (lane / MF) + e;
+                    ++g_checked;
+                    if (got[lane][e] != code(r, k)) fail("fragment value", lane, e, r, k);
+                }
+        }
+    free(lds);
+    free(filled);
 }
 
 int main() {
@@ -121,6 +209,10 @@ int main() {
     // R-contiguous B of the HGEMM workload exactly: 4001 columns, ldb 4008
     check_rc(256, 64, 512, 4001, 4104, 4008, 4160);
     check_rc(256, 64, 256, 4001, 4104, 4008, 4160);
+    // the DMA kernel's tiles: 256 rows, BK 64, 4 waves, both MFMA shapes,
+    // both storage orders
+    for (int mf : {32, 16})
+        for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, 4);
     printf("checked %ld chunk reads, %ld failures\n", g_checked, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -59,8 +59,14 @@ def test_dispatcher_shape_classes(lib):
     assert pick(4096, 4096, 4096).startswith("large")
     assert pick(3999, 4001, 4104).startswith("large")
     assert pick(16384, 16384, 1024).startswith("large")
+    # both operands K-contiguous (A row-major, B column-major): the LDS-DMA
+    # tile with the 16x16x32 MFMA
+    assert names[lg.gemm_select_config(4096, 4096, 4096, R, Cm, F16, F32, F32)] == \
+        "large_dma_256x256x64_w2x2_mfma16x16x32"
+    assert names[lg.gemm_select_config(4096, 4096, 4096, Cm, R, F16, F32, F32)].startswith("large8")
     assert pick(16, 16384, 16384).startswith("skinny")
-    assert pick(256, 256, 256).startswith("small")
+    assert pick(256, 256, 256).startswith("tiny")     # 16 small tiles: 64 tiny ones
+    assert pick(1024, 1024, 1024).startswith("small")
     I8, I32 = lg.GEMM_I8, lg.GEMM_I32
     pick8 = lambda M, N, K: names[lg.gemm_select_config(M, N, K, R, Cm, I8, I32, I32)]
     assert pick8(4096, 4096, 4096).startswith("i8_large8")

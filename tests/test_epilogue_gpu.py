@@ -31,7 +31,12 @@ pytestmark = pytest.mark.gpu
 
 NONE, RELU, GELU = lg.GEMM_ACT_NONE, lg.GEMM_ACT_RELU, lg.GEMM_ACT_GELU
 # tile-table entry -> block tile edge (None: skinny split-K), as in test_gemm_gpu
-ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256}
+ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256, 13: 256, 14: 32, 15: 256}
+VEC_ONLY = {13, 15}   # LDS-DMA entries: 16-byte aligned operand lines only
+
+
+def _align(cid):
+    return 8 if cid in VEC_ONLY else 1
 
 
 def _entry_shape(cid):
@@ -174,7 +179,7 @@ def test_every_entry_gelu_bias_scale(cid, lc, ld):
     ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, layoutC=lc,
                                  layoutD=ld, values="uniform", c_values="normal",
                                  bias_values="normal", alpha=0.75, beta=-0.5, act=GELU,
-                                 seed=5000 + cid)
+                                 seed=5000 + cid, align=_align(cid))
     _check(ep, False, cid, "cfg%d GELU C%d D%d" % (cid, lc, ld))
 
 
@@ -188,7 +193,8 @@ def test_every_entry_relu_integer_exact(cid, out_dt, acc_dt, in_dt):
                                  layoutD=COL_MAJOR if cid % 2 == 0 else ROW_MAJOR,
                                  in_dtype=in_dt, acc_dtype=acc_dt, out_dtype=out_dt,
                                  values="int", c_values="int", bias_values="int",
-                                 alpha=2.0, beta=-1.0, act=RELU, satf=1, seed=5100 + cid)
+                                 alpha=2.0, beta=-1.0, act=RELU, satf=1, seed=5100 + cid,
+                                 align=_align(cid))
     _check(ep, True, cid, "cfg%d ReLU int out=%d" % (cid, out_dt))
 
 
@@ -207,13 +213,13 @@ def test_every_entry_vector_epilogue_with_c_and_bias(cid, out_dt, acc_dt, lcd):
     ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, layoutC=lcd,
                                  layoutD=lcd, out_dtype=out_dt, acc_dtype=acc_dt, values="int",
                                  c_values="int", bias_values="int", alpha=2.0, beta=-1.0,
-                                 act=RELU, ldc=ld, ldd=ld, seed=5300 + cid)
+                                 act=RELU, ldc=ld, ldd=ld, seed=5300 + cid, align=_align(cid))
     _check(ep, True, cid, "cfg%d vector epilogue int out=%d CD%d" % (cid, out_dt, lcd))
     ep = W.make_epilogue_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, layoutC=lcd,
                                  layoutD=lcd, out_dtype=out_dt, acc_dtype=acc_dt,
                                  values="uniform", c_values="normal", bias_values="normal",
                                  alpha=0.75, beta=-0.5, act=GELU, ldc=ld, ldd=ld,
-                                 seed=5350 + cid)
+                                 seed=5350 + cid, align=_align(cid))
     _check(ep, False, cid, "cfg%d vector epilogue GELU out=%d CD%d" % (cid, out_dt, lcd))
 
 
@@ -251,10 +257,10 @@ def test_unaligned_bias_takes_the_element_path():
     _check(ep, True, None, "bias offset 1 float", bias_offset=1)
 
 
-@pytest.mark.parametrize("cid", [0, 1, 4])
+@pytest.mark.parametrize("cid", [0, 1, 4, 13, 15])
 def test_default_epilogue_is_gemm_run(cid):
     prob = W.make_problem(700, 650, 300, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="uniform",
-                          c_values="normal", ldd=656, seed=5600 + cid)
+                          c_values="normal", ldd=656, seed=5600 + cid, align=_align(cid))
     A, B = _dev(prob.A), _dev(prob.B)
     C = _dev(prob.C)
     outs = []

@@ -114,7 +114,15 @@ def test_multi_round_ragged_row_order_raster(values, exact):
 
 # tile-table entries: id -> block tile edge (None: the skinny split-K entry);
 # test_config_ids_match_table checks this against the library's table
-ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256}
+ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256, 13: 256, 14: 32, 15: 256}
+# entries whose kernels load 16-byte aligned operands only (LDS DMA): their
+# sweeps use leading dimensions rounded up to 8 elements (still ragged M, N
+# and K, padding poisoned with NaN)
+VEC_ONLY = {13, 15}
+
+
+def _align(cid):
+    return 8 if cid in VEC_ONLY else 1
 
 
 def _entry_shapes():
@@ -131,6 +139,7 @@ def test_config_ids_match_table():
     # 16-bit entries here; the int8 entries (ids 5..8) and the fp8 entries
     # (ids 9..12) are covered by test_int8_gpu and test_fp8_gpu
     assert lg.gemm_num_configs() == len(ENTRY_TILE) + 8
+    assert lg.gemm_config_name(13).startswith("large_dma")
     for cid in range(5, 9):
         assert lg.gemm_config_name(cid).startswith("i8_")
     for cid in range(9, 13):
@@ -140,7 +149,7 @@ def test_config_ids_match_table():
         if bm is None:
             assert name.startswith("skinny"), name
         else:
-            assert name.split("_")[1].startswith("%dx%d" % (bm, bm)), name
+            assert "_%dx%dx" % (bm, bm) in name, name
 
 
 @pytest.mark.parametrize("cid,M,N,K", _entry_shapes())
@@ -150,7 +159,7 @@ def test_every_entry_layouts_dtypes(cid, M, N, K):
             for lb in (ROW_MAJOR, COL_MAJOR):
                 for values, exact in (("int", True), ("uniform", False)):
                     prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, in_dtype=in_dt,
-                                          values=values, seed=1000 + cid)
+                                          values=values, seed=1000 + cid, align=_align(cid))
                     _full_check(prob, exact, config=cid,
                                 label="cfg%d %dx%dx%d in=%d A%d B%d %s" % (
                                     cid, M, N, K, in_dt, la, lb, values))
@@ -170,7 +179,8 @@ def test_every_entry_output_modes(cid, M, N, K):
             if values == "int" and cv is not None:
                 mode = dict(mode, c_values="int")
             prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
-                                  in_dtype=F16, values=values, seed=2000 + cid, **mode)
+                                  in_dtype=F16, values=values, seed=2000 + cid,
+                                  align=_align(cid), **mode)
             _full_check(prob, exact, config=cid,
                         label="cfg%d out=%d acc=%d inplace=%s %s" % (
                             cid, prob.out_dtype, prob.acc_dtype, prob.inplace, values))
@@ -189,14 +199,16 @@ def test_every_entry_c_on_the_vector_epilogue(cid, out_dt, acc_dt):
         prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, in_dtype=F16,
                               acc_dtype=acc_dt, out_dtype=out_dt, values=values,
                               c_values="int" if exact else "normal", ldc=ld, ldd=ld,
-                              seed=2100 + cid)
+                              seed=2100 + cid, align=_align(cid))
         _full_check(prob, exact, config=cid,
                     label="cfg%d vector C out=%d %s" % (cid, out_dt, values))
 
 
 @pytest.mark.parametrize("cid", sorted(ENTRY_TILE))
 def test_unaligned_leading_dims(cid):
-    # lda, ldb not multiples of 8 elements: the element-wise load path
+    # lda, ldb not multiples of 8 elements: the element-wise load path (an
+    # LDS-DMA entry forced on them is rejected; the dispatcher's choice for
+    # a large unaligned problem falls back to register-staged loads)
     M, N, K = (37, 45, 77) if ENTRY_TILE[cid] is not None else (9, 300, 700)
     for la, lb in ((ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR)):
         a_in = K if la == ROW_MAJOR else M
@@ -204,7 +216,22 @@ def test_unaligned_leading_dims(cid):
         prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, values="int",
                               lda=a_in + 1, ldb=b_in + 3, ldd=N + 2, c_values="int",
                               seed=3000 + cid)
+        if cid in VEC_ONLY:
+            with pytest.raises(lg.GemmError) as e:
+                DeviceProblem(prob).run(config=cid)
+            assert e.value.status == -8
+            continue
         _full_check(prob, True, config=cid, label="cfg%d unaligned A%d B%d" % (cid, la, lb))
+
+
+@pytest.mark.parametrize("values,exact", [("int", True), ("uniform", False)])
+def test_large_unaligned_falls_back_to_staged_loads(values, exact):
+    """A large problem with unaligned lda / ldb: the dispatcher picks the
+    large tile, whose LDS-DMA kernel cannot take these operands; the
+    register-staged large tile runs it (ragged M, N, K; fp32 C)."""
+    prob = W.make_problem(1030, 777, 301, values=values, lda=301 + 3, ldb=777 + 1,
+                          c_values="int" if exact else "normal", ldd=781, seed=3100)
+    _full_check(prob, exact, label="large unaligned %s" % values)
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 7, 3), (5, 1, 9), (17, 33, 8), (31, 15, 9),
