@@ -1174,8 +1174,15 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     constexpr int KCH = CF::KSTEP * 2 / 16;       // 16-byte chunks per step (KC reads)
     static_assert(CF::ES == 2 && CF::FC == 1, "16-bit operands");
     static_assert(BK == 64, "LDS rows of 128 bytes (KC layout)");
+    // B_REG (row-major B with row-major A): B is loaded into registers and
+    // transposed on its way to LDS by LoaderRC, so LDS holds it K-contiguous
+    // like A; a transposed LDS read of B costs more than that register
+    // transpose (measured).  Column-major A keeps the transposed reads.
+    constexpr bool B_REG = A_KC && !B_KC;
+    constexpr bool B_KCL = B_KC || B_REG;  // B's LDS tile is K-contiguous
     using DA = DmaOperand<BM, BK, NWAVES, MF, A_KC, RAGGED>;
-    using DB = DmaOperand<BN, BK, NWAVES, MF, B_KC, RAGGED>;
+    using DB = DmaOperand<BN, BK, NWAVES, MF, B_KCL, RAGGED>;
+    using LB = LoaderRC<BN, BK, CF::THREADS>;
     constexpr int SA = DA::BYTES, SB = DB::BYTES;  // bytes per stage
     char *const ldsA = lds, *const ldsB = lds + 2 * SA;
 
@@ -1187,8 +1194,10 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
     DA da;
     DB db;
+    LB lb;
     da.init(lane, wave, m0, p.M, p.lda);
-    db.init(lane, wave, n0, p.N, p.ldb);
+    if constexpr (B_REG) lb.init(tid, p.ldb, n0, p.N);
+    else db.init(lane, wave, n0, p.N, p.ldb);
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)p.a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb =
@@ -1202,7 +1211,15 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     };
     auto zero_ragged = [&](int stage, int k0) {  // the tile at k0 is the ragged last one
         DA::zero_tail(ldsA + stage * SA, kend - k0, tid, CF::THREADS);
-        DB::zero_tail(ldsB + stage * SB, kend - k0, tid, CF::THREADS);
+        if constexpr (!B_REG) DB::zero_tail(ldsB + stage * SB, kend - k0, tid, CF::THREADS);
+    };
+    // B_REG: the register loads of B's tile at k0, and its transposing
+    // stores into a stage (k >= kend masked to zero in RAGGED kernels; the
+    // mask is a no-op on full tiles and keeps the loop free of branches)
+    auto b_store = [&](int stage, int k0, auto w_tag) {
+        constexpr int w = decltype(w_tag)::value;
+        if constexpr (RAGGED && w == 0) lb.mask(k0, kend);
+        lb.template store_one<w>(reinterpret_cast<u32x4 *>(ldsB + stage * SB), tid);
     };
 
     // per-lane LDS byte offsets of each fragment at step 0, stage 0
@@ -1220,7 +1237,7 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int rb0 = wn * CF::WTN + j * MF;
-        if constexpr (B_KC) {
+        if constexpr (B_KCL) {
             const int r = rb0 + (lane & (MF - 1));
             b_off[j] = (uint32_t)(r * DB::CH + ((lane / MF) ^ swz_kc(r))) * 16u;
         } else {
@@ -1234,7 +1251,7 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         constexpr int ks = decltype(ks_tag)::value, sl = decltype(sl_tag)::value;
         constexpr int f = decltype(f_tag)::value;
         constexpr bool isA = f < TM;
-        constexpr bool kc = isA ? A_KC : B_KC;
+        constexpr bool kc = isA ? A_KC : B_KCL;
         constexpr int RB = isA ? BM * 2 : BN * 2;  // R-contiguous: bytes per k-row
         const char *base;
         uint32_t off;
@@ -1270,16 +1287,24 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         else acc[i][j] = mfma16<IT, 1>(xb, xa, acc[i][j]);
     };
 
-    // prologue: tiles 0 and 1 in flight, wait for tile 0, its step-0 fragments
-    constexpr int NDMA = DA::NI + DB::NI;
+    // prologue: tiles 0 and 1 in flight, wait for tile 0, its step-0
+    // fragments (B_REG: B of tile 0 stored; B of tile 1 loaded into the
+    // registers before A's DMA of tile 1, the order the loop keeps)
+    constexpr int NDMA = DA::NI + (B_REG ? 0 : DB::NI);  // DMA instructions per wave and tile
+    constexpr int NBL = B_REG ? LB::NLOAD : 0;             // B register loads per thread and tile
 #pragma unroll
     for (int g = 0; g < NDMA; ++g) dma_one(g, 0, kbeg, true);
+    if constexpr (B_REG) {
+        lb.template load<RAGGED>(rb, kbeg, p.ldb, kend);
+        Unroll<0, LB::NSTORE>::run([&](auto w) { b_store(0, kbeg, w); });
+        lb.template load<RAGGED>(rb, kbeg + min(1, nk - 1) * BK, p.ldb, kend);
+    }
     if (nk > 1) {
 #pragma unroll
         for (int g = 0; g < NDMA; ++g) dma_one(g, 1, kbeg + BK, true);
-        wait_vmcnt<NDMA>();
+        wait_vmcnt<NDMA + NBL>();
     } else {
-        wait_vmcnt<0>();
+        wait_vmcnt<NBL>();
     }
     __syncthreads();
     if constexpr (RAGGED) {
@@ -1299,12 +1324,15 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         // (from the last tile's addresses), so the loop body has no branch
         const bool more = t + 2 < nk;
         const int k_pre = kbeg + min(t + 2, nk - 1) * BK;
+        const int k_next = kbeg + min(t + 1, nk - 1) * BK;  // B_REG: the tile stored in step 0
         Unroll<0, KS>::run([&](auto ks_tag) {
             constexpr int ks = decltype(ks_tag)::value;
             constexpr int sl = ks & 1;
             if constexpr (ks == KS - 1) {
                 // tile t+1 has landed everywhere; stage cur is no longer read
-                wait_vmcnt<0>();
+                // (B_REG: B's loads of tile t+2, issued in step 0, stay in
+                // flight; the counter retires in order)
+                wait_vmcnt<NBL>();
                 __syncthreads();
                 if constexpr (RAGGED) {
                     if (t + 1 < nk && kbeg + (t + 2) * BK > kend) {
@@ -1326,6 +1354,15 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
                         constexpr int g = decltype(g_tag)::value;
                         if constexpr (g * NM / NDMA == m) dma_one(g, cur, k_pre, more);
                     });
+                }
+                if constexpr (B_REG && ks == 0) {
+                    // B of tile t+1 (loaded one tile ago) into its stage, one
+                    // store per MFMA; then the loads of tile t+2 into the
+                    // freed registers (past the last tile: the last one again)
+                    if constexpr (m < LB::NSTORE)
+                        b_store(cur ^ 1, k_next, std::integral_constant<int, m>{});
+                    else if constexpr (m - LB::NSTORE < LB::NLOAD)
+                        lb.template load_one<m - LB::NSTORE, RAGGED>(rb, k_pre, p.ldb, kend);
                 }
                 auto read_next = [&](auto fq) {
                     if constexpr (ks + 1 < KS)
