@@ -35,13 +35,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s (2MNK/t) and % of MI355X fp16 MFMA peak, 4096³ fp16→fp32"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_4096_f16.json")
 COPY_BYTES = 256 << 20  # size of the calibration copy
 
 
-def load_traffic():
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, while the kernel sources are the ones it was taken from."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -128,10 +133,10 @@ WORKLOADS = {
 # the measured ceilings (libgemm_measure): name -> (description, unit)
 MEASURE_WORKLOADS = {
     "mfma_peak_32": ("MFMA stream: independent v_mfma_f32_32x32x16_f16 on random fp16 operands "
-                     "held in registers, 4 waves (one per SIMD) per CU, no memory traffic",
+                     "held in registers, 8 waves (two per SIMD) per CU, no memory traffic",
                      "TFLOP/s"),
     "mfma_peak_16": ("MFMA stream: independent v_mfma_f32_16x16x32_f16 on random fp16 operands "
-                     "held in registers, 4 waves (one per SIMD) per CU, no memory traffic",
+                     "held in registers, 8 waves (two per SIMD) per CU, no memory traffic",
                      "TFLOP/s"),
     "copy": ("device copy of 512 MiB with 16-byte loads and stores (read + write bytes)", "GB/s"),
 }
@@ -308,7 +313,7 @@ def main():
     flop = float(prob.flops)
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (mean_ms * 1e-3) / 1e12
-    traffic = load_traffic() if args.workload == "4096_f16" else None
+    traffic = load_traffic(args.workload)
     nbytes = algorithmic_bytes(prob)
     if bound == "mfma_fp8":
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
@@ -352,7 +357,7 @@ def main():
         "roofline": dict(roof, **{
             "traffic": traffic,
             "algorithmic_bytes": nbytes,
-            "kernel": "gemm_mfma_kernel<%s>" % lg.gemm_config_name(cfg),
+            "kernel": "libgemm entry %s" % lg.gemm_config_name(cfg),
             "launch_ms_mean": round(mean_ms, 5),
             "launch_ms_min": round(min(durations_ms), 5),
             "launch_ms_median": round(sorted(durations_ms)[len(durations_ms) // 2], 5),
@@ -391,7 +396,7 @@ def measure(args):
         rng = np.random.default_rng(20260)
         ops = (rng.random(32768, dtype=np.float32) * 2 - 1).astype(np.float16)   # 64 KiB
         operands = torch.from_numpy(ops.view(np.int16)).to(dev)
-        blocks, threads, iters = cus, 256, 20000
+        blocks, threads, iters = cus, 512, 10000
         out = torch.empty(blocks * threads, dtype=torch.float32, device=dev)
         work = float(lib.gemm_measure_mfma_flops(mf, blocks, threads, iters))
 
