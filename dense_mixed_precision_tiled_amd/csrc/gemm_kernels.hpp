@@ -657,16 +657,25 @@ __device__ __forceinline__ float from_out16(uint32_t h) {
 // result rounded once to OUT, satf applied and the group stored.  FULL: the
 // group lies inside M x N and C/D/bias allow 4-element vector access, so no
 // checks; else each element is checked and stored alone.
-// C(i, j..j+3) of a group inside M x N with vector-friendly row-major C, as
-// fp32 values (float outputs only).
+// C(i, j..j+3) of a group inside M x N with vector-friendly row-major C (float
+// outputs only), as raw bits (fp32: 4 words; 16-bit: 2 words of two values
+// each), so that a batch of loads holds half the registers until its values
+// are used; c_from_raw converts them to fp32.
 template <int OUT>
-__device__ __forceinline__ f32x4 load_c4(const Params &p, int i, int j) {
+__device__ __forceinline__ auto load_c_raw(const Params &p, int i, int j) {
     if constexpr (OUT == DT_F32) {
-        return *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.C) +
+        return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(p.C) +
                                                 (int64_t)i * p.ldc + j);
     } else {
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(
-            reinterpret_cast<const uint16_t *>(p.C) + (int64_t)i * p.ldc + j);
+        return *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint16_t *>(p.C) +
+                                                (int64_t)i * p.ldc + j);
+    }
+}
+template <int OUT, class Raw>
+__device__ __forceinline__ f32x4 c_from_raw(const Raw &w) {
+    if constexpr (OUT == DT_F32) {
+        return __builtin_bit_cast(f32x4, w);
+    } else {
         return f32x4{from_out16<OUT>(lo16(w[0])), from_out16<OUT>(hi16(w[0])),
                      from_out16<OUT>(lo16(w[1])), from_out16<OUT>(hi16(w[1]))};
     }
@@ -1430,6 +1439,10 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
     // edge, or unaligned / column-major C and D, go element by element.
     constexpr int NG = AccT<MF>::N / 4;  // 4-column groups per MFMA tile and lane
     const bool full = (m0 + BM <= p.M) && (n0 + BN <= p.N) && p.cd_vec && p.splits == 1;
+    // every tile of a float output (at the M edge rows >= M are skipped, at
+    // the N edge groups past N; int8 kernels, whose epilogue holds no C ahead,
+    // take interior tiles only: the checks cost them spills)
+    const bool ncols = IT == IT_I8 ? full : p.cd_vec && p.splits == 1;
     // (Edge tiles go through the staged loop below, which stores every group
     // inside M x N with vector stores too.  Handling them here, with a bounds
     // check and an element-wise fallback per group, made this unrolled code
@@ -1437,42 +1450,89 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
     // 16384^2 x 1024 shape, 16 tiles per CU, 25%.)
     auto direct = [&](auto out_tag) {
         constexpr int OUT = decltype(out_tag)::value;
-        // Float outputs load C for a whole row block before the block's
-        // stores: a wait for a load also waits for every earlier store, so
-        // per-group loads would serialise the block.
+        // Float outputs load C ahead of the stores, for RB row blocks at a
+        // time: a wait for a load also waits for every earlier store, so
+        // loads issued between stores serialise them.  RB row blocks of C
+        // take at most 64 registers (all of a wave's C when it is 16-bit).
         constexpr bool PRE = OUT != DT_I32;
-        Unroll<0, TM>::run([&](auto ii) {
-            constexpr int i = decltype(ii)::value;
-            const int row = m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane);
-            auto col_of = [&](int j, int g) {
-                return n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
-            };
-            f32x4 cpre[TN][NG];
+        constexpr int CW = (OUT == DT_F32) ? 4 : 2;  // registers per 4-column group of C
+        constexpr int RB0 = 64 / (TN * NG * CW) < 1 ? 1 : 64 / (TN * NG * CW);
+        constexpr int RB = RB0 >= TM ? TM : (TM % RB0 == 0 ? RB0 : 1);
+        auto col_of = [&](int j, int g) {
+            return n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
+        };
+        auto row_of = [&](int i) { return m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane); };
+        Unroll<0, TM / RB>::run([&](auto bb) {
+            constexpr int i0 = decltype(bb)::value * RB;
+            // raw C bits (fp32: 4 words per group, 16-bit: 2), converted at the store
+            using Raw = typename std::conditional<OUT == DT_F32, u32x4, u32x2>::type;
+            Raw cpre[RB][TN][NG];
             if constexpr (PRE) {
-                Unroll<0, TN>::run([&](auto jj) {
-                    Unroll<0, NG>::run([&](auto gg) {
-                        constexpr int j = decltype(jj)::value, g = decltype(gg)::value;
-                        cpre[j][g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        if (p.C) cpre[j][g] = load_c4<OUT>(p, row, col_of(j, g));
+                Unroll<0, RB>::run([&](auto rr) {
+                    Unroll<0, TN>::run([&](auto jj) {
+                        Unroll<0, NG>::run([&](auto gg) {
+                            constexpr int r = decltype(rr)::value, j = decltype(jj)::value;
+                            constexpr int g = decltype(gg)::value;
+                            const int row = row_of(i0 + r), col = col_of(j, g);
+                            const bool in = row < p.M && col + 4 <= p.N;
+                            cpre[r][j][g] = Raw{};
+                            if (p.C) cpre[r][j][g] = load_c_raw<OUT>(p, in ? row : 0, in ? col : 0);
+                        });
                     });
                 });
             }
-            Unroll<0, TN>::run([&](auto jj) {
-                constexpr int j = decltype(jj)::value;
-                Unroll<0, NG>::run([&](auto gg) {
-                    constexpr int g = decltype(gg)::value;
-                    const int col = col_of(j, g);
-                    const f32x4 v = acc_group<AGPR>(acc[i][j], g);
-                    if constexpr (PRE) finish4<OUT, true, false, true>(p, row, col, v + cpre[j][g]);
-                    else finish4<OUT, true, false>(p, row, col, v);
+            Unroll<0, RB>::run([&](auto rr) {
+                constexpr int r = decltype(rr)::value, i = i0 + r;
+                const int row = row_of(i);
+                if constexpr (IT != IT_I8) {
+                    if (row >= p.M) return;
+                }
+                Unroll<0, TN>::run([&](auto jj) {
+                    constexpr int j = decltype(jj)::value;
+                    Unroll<0, NG>::run([&](auto gg) {
+                        constexpr int g = decltype(gg)::value;
+                        const int col = col_of(j, g);
+                        const f32x4 v = acc_group<AGPR>(acc[i][j], g);
+                        if constexpr (IT == IT_I8) {
+                            finish4<OUT, true, false>(p, row, col, v);
+                        } else if (col + 4 <= p.N) {
+                            finish4<OUT, true, false, true>(p, row, col,
+                                                            v + c_from_raw<OUT>(cpre[r][j][g]));
+                        }
+                    });
                 });
             });
         });
+        // At the N edge, the lane's group that crosses it (column pc, the same
+        // in every row the lane holds): gathered from the accumulators by
+        // selects, finished element-wise once per row
+        if constexpr (IT != IT_I8) {
+            if (!full && n0 + BN > p.N) {
+                int pc = -1;
+                Unroll<0, TN>::run([&](auto jj) {
+                    Unroll<0, NG>::run([&](auto gg) {
+                        const int c = col_of(decltype(jj)::value, decltype(gg)::value);
+                        if (c < p.N && c + 4 > p.N) pc = c;
+                    });
+                });
+                Unroll<0, TM>::run([&](auto ii) {
+                    constexpr int i = decltype(ii)::value;
+                    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+                    Unroll<0, TN>::run([&](auto jj) {
+                        Unroll<0, NG>::run([&](auto gg) {
+                            constexpr int j = decltype(jj)::value, g = decltype(gg)::value;
+                            if (col_of(j, g) == pc) v = acc_group<AGPR>(acc[i][j], g);
+                        });
+                    });
+                    if (pc >= 0) finish4<OUT, false, false>(p, row_of(i), pc, v);
+                });
+            }
+        }
     };
     // (kernels with element-wise operand loads serve unaligned operands, a
     // slow path anyway: they finish through the staged loop only)
     if constexpr (VEC) {
-        if (full && !p.epi) {
+        if (ncols && !p.epi) {
             if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{});
             else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
             else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
