@@ -129,6 +129,11 @@ WORKLOADS = {
     # OCP fp8 E4M3 inputs, fp32 accumulate
     "4096_fp8": (None, "M=N=K=4096 GEMM, fp8 E4M3 A row-major and B column-major "
                  "(uniform[-1,1] rounded to E4M3), fp32 accumulate and D, C=0", "mfma_fp8"),
+    # the same with row-major B (N-contiguous, transposed on the way to LDS)
+    "4096_i8_rowB": (None, "M=N=K=4096 GEMM, int8 A and B row-major (uniform over "
+                     "[-128,127]), int32 accumulate and D, C=0", "mfma_i8"),
+    "4096_fp8_rowB": (None, "M=N=K=4096 GEMM, fp8 E4M3 A and B row-major (uniform[-1,1] "
+                      "rounded to E4M3), fp32 accumulate and D, C=0", "mfma_fp8"),
 }
 # the measured ceilings (libgemm_measure): name -> (description, unit)
 MEASURE_WORKLOADS = {
@@ -157,6 +162,12 @@ def make_workload(W, name):
                               values="uniform", seed=20360)
     elif name == "4096_i8":
         prob = W.make_int8_problem(4096, 4096, 4096, values="full", c_values=None, seed=20350)
+    elif name == "4096_i8_rowB":
+        prob = W.make_int8_problem(4096, 4096, 4096, layoutB=0, values="full", c_values=None,
+                                   seed=20370)
+    elif name == "4096_fp8_rowB":
+        prob = W.make_problem(4096, 4096, 4096, layoutA=0, layoutB=0, in_dtype=W.FP8_E4M3,
+                              values="uniform", seed=20380)
     elif name == "4096_f16_colD":
         prob = W.make_epilogue_problem(4096, 4096, 4096, layoutD=1, values="uniform",
                                        c_values=None, bias_values=None, ldd=4096, seed=20340)

@@ -53,6 +53,25 @@ LIBGEMM_HD inline int64_t rc_chunk_offset(int r, int k, int R, int kend, int64_t
     return ((int64_t)kk * ld + rr) * 2;
 }
 
+// R-contiguous storage of 8-bit elements: byte offset of the dword holding
+// X(r..r+3, k), with the 4-aligned column r clamped to the dword holding
+// column R-1 and, when clampk, k clamped to kend-1.
+LIBGEMM_HD inline int64_t rc8_dword_offset(int r, int k, int R, int kend, int64_t ld,
+                                           bool clampk) {
+    const int rr = imin(r, (R - 1) & ~3);
+    const int kk = clampk ? imin(k, kend - 1) : k;
+    return (int64_t)kk * ld + rr;
+}
+
+// The in-register transpose of an R-contiguous 8-bit block (4 rows x 16
+// k-rows, one dword per k-row): dword d of row e's K-contiguous chunk holds
+// byte e of the k-rows 4d..4d+3 (a..d), k-row 4d in byte 0.
+LIBGEMM_HD inline uint32_t rc8_gather(uint32_t a, uint32_t b, uint32_t c, uint32_t d, int e) {
+    const int s = 8 * e;
+    return ((a >> s) & 0xffu) | (((b >> s) & 0xffu) << 8) | (((c >> s) & 0xffu) << 16) |
+           (((d >> s) & 0xffu) << 24);
+}
+
 // The byte extent the vector path allows: the operand's last element, rounded
 // up to 16 bytes (outer lines of inner elements at stride ld).
 LIBGEMM_HD inline int64_t operand_range(int64_t outer, int64_t inner, int64_t ld, int es) {

@@ -325,8 +325,7 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     p.epi = (epi.alpha != 1.0f || (C && epi.beta != 1.0f) || epi.bias ||
              epi.activation != GEMM_ACT_NONE || p.c_col) ? 1 : 0;
     // Vector path: 16-byte aligned operands (lines a multiple of 16 bytes)
-    // whose extents, rounded up to 16 bytes, fit a 32-bit buffer range; int8
-    // operands must also be K-contiguous (A row-major, B column-major)
+    // whose extents, rounded up to 16 bytes, fit a 32-bit buffer range
     const int isz = in_size(in_dtype);
     const int64_t a_ext =
         (layoutA == GEMM_ROW_MAJOR ? (M - 1) * lda + K : (K - 1) * lda + M) * isz;
@@ -335,9 +334,7 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const int64_t a_rng = (a_ext + 15) & ~(int64_t)15, b_rng = (b_ext + 15) & ~(int64_t)15;
     p.vec_ok = K > 0 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
                ((lda * isz) % 16 == 0) && ((ldb * isz) % 16 == 0) &&
-               a_rng < ((int64_t)1 << 32) - 16 && b_rng < ((int64_t)1 << 32) - 16 &&
-               (isz == 2 || (layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR));
-    // (the 8-bit vector loads need K-contiguous A and B: A row-major, B col-major)
+               a_rng < ((int64_t)1 << 32) - 16 && b_rng < ((int64_t)1 << 32) - 16;
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
     if (needs_vec(id) && !p.vec_ok) {

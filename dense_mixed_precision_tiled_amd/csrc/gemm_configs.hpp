@@ -109,18 +109,12 @@ template <class CF, int IT, bool AKC, bool BKC>
 hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
     // the K loop masks k >= kend only when some slice ends inside a K-tile
     const bool ragged = (p.K % CF::BK) != 0 || (p.k_per_split % CF::BK) != 0;
-    // int8 vector loads need both operands K-contiguous (the host's vec_ok
-    // says so); other int8 layouts take the element-wise loads
-    constexpr bool can_vec = CF::ES == 2 || (AKC && BKC);
     const dim3 block(CF::THREADS);
-    if (!can_vec || !p.vec_ok)
+    if (!p.vec_ok)
         return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, false, false>, grid, block, p, s);
-    if constexpr (can_vec) {
-        if (ragged)
-            return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, true>, grid, block, p, s);
-        return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, false>, grid, block, p, s);
-    }
-    return hipErrorInvalidValue;  // not reached
+    if (ragged)
+        return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, true>, grid, block, p, s);
+    return launch_params(gemm_mfma_kernel<CF, IT, AKC, BKC, true, false>, grid, block, p, s);
 }
 
 // LDS-DMA kernels: vector operands only (the host never sends others here).

@@ -197,6 +197,10 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff,
                                                                             (int)soff, 0));
 }
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                             uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)voff, (int)soff, 0);
+}
 
 template <int ROWS, int BK, int THREADS, int ES = 2>
 struct LoaderKC {
@@ -206,6 +210,7 @@ struct LoaderKC {
     static constexpr bool PARTIAL = TOTAL < THREADS;
     static constexpr int PER = PARTIAL ? 1 : TOTAL / THREADS;
     static constexpr int NLOAD = PER, NSTORE = PER;
+    static constexpr int SPB = 1, LPB = 1;  // stores and loads per block (a chunk)
     static_assert(PARTIAL || TOTAL % THREADS == 0, "tile/threads");
     static_assert(PARTIAL || THREADS % CH == 0, "threads/chunks");
     u32x4 v[PER];
@@ -311,6 +316,7 @@ struct LoaderRC {
     static constexpr int NBLK = PERT / KB;           // blocks per thread
     static constexpr int NBLOCKS = TOTAL / KB;       // blocks in the tile
     static constexpr int NLOAD = NBLK * KB, NSTORE = NBLK * 8;
+    static constexpr int SPB = 8, LPB = KB;  // stores and loads per block
     static_assert(PARTIAL || TOTAL % THREADS == 0, "tile/threads");
     static_assert(KB == 1 || KB == 2 || KB == 4 || KB == 8, "k-depth");
     static_assert(PERT % KB == 0, "blocks");
@@ -445,6 +451,92 @@ struct LoaderRC {
         for (int j = 0; j < NBLK; ++j)
 #pragma unroll
             for (int e = 0; e < 8; ++e) store_col(lds, tid, j, e);
+    }
+};
+
+// R-contiguous 8-bit operand (row-major B or column-major A of int8 / fp8):
+// blocks of 4 consecutive rows r x 16 k-rows, one dword load per k-row (the
+// lanes of a wave cover consecutive 4-row groups, so one load instruction
+// reads a contiguous stretch of a k-row), transposed in registers into the
+// 16-byte K-contiguous chunks of the 4 rows (rc8_gather), which go to LDS
+// like the K-contiguous loader's.  A tile with fewer blocks than threads has
+// threads repeat blocks (identical stores).
+template <int ROWS, int BK, int THREADS>
+struct LoaderRC8 {
+    static constexpr int CH = BK / 16;             // 16-byte chunks per LDS row
+    static constexpr int RG = ROWS / 4;             // 4-row groups
+    static constexpr int TOTAL = RG * (BK / 16);    // blocks in the tile
+    static constexpr bool PARTIAL = TOTAL < THREADS;
+    static constexpr int NBLK = PARTIAL ? 1 : TOTAL / THREADS;
+    static constexpr int NLOAD = NBLK * 16, NSTORE = NBLK * 4;
+    static constexpr int SPB = 4, LPB = 16;         // stores and loads per block
+    static_assert(ROWS % 4 == 0 && BK % 16 == 0, "4-row groups, 16 k-rows per block");
+    static_assert(PARTIAL || TOTAL % THREADS == 0, "tile/threads");
+    static_assert(PARTIAL || THREADS % RG == 0, "threads/row groups");
+    uint32_t v[NBLK][16];  // v[j][kk]: rows 4rg..4rg+3 at k = 16*kg_j + kk
+    uint32_t voff;         // byte offset of this thread's row group at k = 0
+    int rg;                // the row group (the same for every j)
+    int kg[NBLK];          // k-group of each block
+
+    __device__ __forceinline__ static int block(int j, int tid) {
+        return PARTIAL ? tid % TOTAL : j * THREADS + tid;
+    }
+
+    __device__ __forceinline__ void init(int tid, int64_t ld, int r0, int R) {
+        rg = block(0, tid) % RG;
+        voff = (uint32_t)rc8_dword_offset(r0 + rg * 4, 0, R, 1, ld, false);
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) kg[j] = block(j, tid) / RG;
+    }
+
+    // CLAMPK: the k-row goes into the per-lane offset, clamped to kend-1;
+    // otherwise the K-tile's start rides in the scalar offset
+    template <bool CLAMPK>
+    __device__ __forceinline__ uint32_t load_at(__amdgpu_buffer_rsrc_t rsrc, int j, int kk, int k0,
+                                                int64_t ld, int kend) const {
+        const uint32_t l = (uint32_t)ld;
+        if constexpr (CLAMPK)
+            return buf_load4(rsrc, voff + (uint32_t)imin(k0 + kg[j] * 16 + kk, kend - 1) * l, 0u);
+        else
+            return buf_load4(rsrc, voff + (uint32_t)(kg[j] * 16 + kk) * l, (uint32_t)k0 * l);
+    }
+
+    template <bool CLAMPK>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld, int kend) {
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) v[j][kk] = load_at<CLAMPK>(rsrc, j, kk, k0, ld, kend);
+    }
+
+    template <int idx, bool CLAMPK>
+    __device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t rsrc, int k0, int64_t ld,
+                                             int kend) {
+        v[idx / 16][idx % 16] = load_at<CLAMPK>(rsrc, idx / 16, idx % 16, k0, ld, kend);
+    }
+
+    __device__ __forceinline__ void mask(int k0, int kend) {
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk)
+                if (k0 + kg[j] * 16 + kk >= kend) v[j][kk] = 0u;
+    }
+
+    // the idx-th LDS store: block idx / 4, row 4rg + idx % 4
+    template <int idx>
+    __device__ __forceinline__ void store_one(u32x4 *lds, int tid) const {
+        constexpr int j = idx / 4, e = idx % 4;
+        u32x4 w;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            w[d] = rc8_gather(v[j][4 * d], v[j][4 * d + 1], v[j][4 * d + 2], v[j][4 * d + 3], e);
+        const int r = rg * 4 + e;
+        lds[r * CH + (kg[j] ^ swz(r))] = w;
+    }
+
+    __device__ __forceinline__ void store(u32x4 *lds, int tid) const {
+        Unroll<0, NSTORE>::run([&](auto w) { store_one<decltype(w)::value>(lds, tid); });
     }
 };
 
@@ -833,6 +925,16 @@ __device__ __forceinline__ void map_tile(const Params &p, int w, int &tm, int &t
 // two tiles later and the stores of tile t+1 before its reads.  The body has
 // no branches: past the last K-tile the loads re-read it and the stores and
 // reads go to the idle stage.
+// The loader of one operand tile: K-contiguous operands load chunks as
+// stored; R-contiguous ones are transposed in registers (16-bit: LoaderRC,
+// 8-bit: LoaderRC8).  The element-wise path (VEC false) gathers K-contiguous
+// chunks by layout (LoaderKC::load_checked; LoaderRC's for 16-bit).
+template <class CF, int ROWS, bool KC, bool VEC>
+using OperandLoader = typename std::conditional<
+    KC || (CF::ES == 1 && !VEC), LoaderKC<ROWS, CF::BK, CF::THREADS, CF::ES>,
+    typename std::conditional<CF::ES == 1, LoaderRC8<ROWS, CF::BK, CF::THREADS>,
+                              LoaderRC<ROWS, CF::BK, CF::THREADS>>::type>::type;
+
 template <class CF, int IT, bool A_KC, bool B_KC, bool VEC, bool RAGGED>
 __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg, int kend,
                                        typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
@@ -844,13 +946,8 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
     static_assert(KS % 2 == 0 && KS >= 2, "fragment slots alternate across K-tiles; the"
                   " store and barrier steps are distinct");
     constexpr int FC = CF::FC;  // 16-byte chunks per lane and operand fragment
-    // 8-bit operands always use K-contiguous chunks: the vector path needs
-    // K-contiguous storage, the element-wise path gathers by layout
-    static_assert(CF::ES == 2 || !VEC || (A_KC && B_KC), "int8 vector loads need K-contiguous A, B");
-    using LA = typename std::conditional<A_KC || CF::ES == 1, LoaderKC<BM, BK, THREADS, CF::ES>,
-                                         LoaderRC<BM, BK, THREADS>>::type;
-    using LB = typename std::conditional<B_KC || CF::ES == 1, LoaderKC<BN, BK, THREADS, CF::ES>,
-                                         LoaderRC<BN, BK, THREADS>>::type;
+    using LA = OperandLoader<CF, BM, A_KC, VEC>;
+    using LB = OperandLoader<CF, BN, B_KC, VEC>;
 
     const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
     if (nk <= 0) return;
@@ -1000,22 +1097,19 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
                         constexpr int w = decltype(w_tag)::value;
                         if constexpr (w * NSLOT / NW == slot) {
                             store_one(cur ^ 1, w_tag);
+                            // a block's loads follow its last store (K-contiguous:
+                            // one store and one load per block)
                             if constexpr (w < LA::NSTORE) {
-                                if constexpr (A_KC) {
-                                    load_one(k_next, w_tag);
-                                } else if constexpr (w % 8 == 7) {
-                                    Unroll<(w / 8) * LA::KB, (w / 8 + 1) * LA::KB>::run(
+                                constexpr int S = LA::SPB, L = LA::LPB;
+                                if constexpr (w % S == S - 1)
+                                    Unroll<(w / S) * L, (w / S + 1) * L>::run(
                                         [&](auto g) { load_one(k_next, g); });
-                                }
                             } else {
                                 constexpr int wb = w - LA::NSTORE;
-                                if constexpr (B_KC) {
-                                    load_one(k_next, std::integral_constant<int, LA::NLOAD + wb>{});
-                                } else if constexpr (wb % 8 == 7) {
-                                    Unroll<LA::NLOAD + (wb / 8) * LB::KB,
-                                           LA::NLOAD + (wb / 8 + 1) * LB::KB>::run(
+                                constexpr int S = LB::SPB, L = LB::LPB;
+                                if constexpr (wb % S == S - 1)
+                                    Unroll<LA::NLOAD + (wb / S) * L, LA::NLOAD + (wb / S + 1) * L>::run(
                                         [&](auto g) { load_one(k_next, g); });
-                                }
                             }
                         }
                     });

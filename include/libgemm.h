@@ -130,10 +130,10 @@ typedef enum {
  * Faults inside the kernels surface at the next synchronisation of the
  * stream.
  *
- * Speed: 16-byte vector loads are used where A and B base pointers are
- * 16-byte aligned and lda, ldb are multiples of 16 bytes (the pages' ldm
- * rule), for int8 and fp8 only with A row-major and B column-major (both
- * K-contiguous); anything else runs correct element-wise loads.  C and D
+ * Speed: vector loads are used where A and B base pointers are 16-byte
+ * aligned and lda, ldb are multiples of 16 bytes (the pages' ldm rule), in
+ * every layout (operands contiguous along M or N are transposed on the way
+ * to LDS); anything else runs correct element-wise loads.  C and D
  * are read and written four elements at a time where their base pointers
  * are aligned to four elements, ldc and ldd are multiples of 4 and C is
  * row-major (and, for gemm_run_ex, a per-column bias is 16-byte aligned);

@@ -115,6 +115,81 @@ static void check_rc(int ROWS, int BK, int THREADS, int R, int K, int64_t ld, in
         }
 }
 
+// R-contiguous loader (8-bit): blocks of 4 rows x 16 k-rows, one dword per
+// k-row, then the in-register transpose (rc8_gather) into the 4 rows'
+// K-contiguous chunks.  Checks the dword reads like check_rc, the block map,
+// and that the transposed chunk of row r at k-group kg holds X(r, 16kg..+15).
+static uint8_t code8(int64_t off) { return (uint8_t)((off * 2654435761u) >> 13); }
+
+static void check_rc8(int ROWS, int BK, int THREADS, int R, int K, int64_t ld, int kps) {
+    const int RG = ROWS / 4, KG = BK / 16;
+    const int TOTAL = RG * KG;
+    const bool partial = TOTAL < THREADS;
+    const int NBLK = partial ? 1 : TOTAL / THREADS;
+    {   // every block covered; the row group the same for all of a thread's blocks
+        char *seen = (char *)calloc(TOTAL, 1);
+        for (int tid = 0; tid < THREADS; ++tid)
+            for (int j = 0; j < NBLK; ++j) {
+                const int b = partial ? tid % TOTAL : j * THREADS + tid;
+                const int b0 = partial ? tid % TOTAL : tid;
+                if (b % RG != b0 % RG) fail("rc8 row group differs across blocks", tid, j, ROWS, BK);
+                if (b < 0 || b >= TOTAL) fail("rc8 block out of range", tid, j, b, TOTAL);
+                else seen[b] = 1;
+            }
+        for (int id = 0; id < TOTAL; ++id)
+            if (!seen[id]) fail("rc8 block not covered", id, ROWS, BK, THREADS);
+        free(seen);
+    }
+    const int64_t range = operand_range(K, R, ld, 1);
+    const int splits = (K + kps - 1) / kps;
+    const bool ragged = (K % BK) != 0 || (kps % BK) != 0;
+    for (int r0 = 0; r0 < R; r0 += ROWS)
+        for (int z = 0; z < splits; ++z) {
+            const int kbeg = z * kps, kend = K < kbeg + kps ? K : kbeg + kps;
+            for (int k0 = kbeg; k0 < kend; k0 += BK)
+                for (int tid = 0; tid < THREADS; ++tid)
+                    for (int j = 0; j < NBLK; ++j) {
+                        const int b = partial ? tid % TOTAL : j * THREADS + tid;
+                        const int rg = b % RG, kg = b / RG;
+                        const int col = r0 + rg * 4;
+                        const int64_t voff = rc8_dword_offset(col, 0, R, 1, ld, false);
+                        uint32_t v[16];
+                        for (int kk = 0; kk < 16; ++kk) {
+                            const int k = k0 + kg * 16 + kk;
+                            const int64_t off = ragged ? voff + (int64_t)imin(k, kend - 1) * ld
+                                                       : voff + (int64_t)(kg * 16 + kk) * ld +
+                                                             (int64_t)k0 * ld;
+                            ++g_checked;
+                            if (off < 0 || off % 4 != 0 || off + 4 > range)
+                                fail("rc8 out of range", off, range, col, k);
+                            const int64_t row = off / ld, c0 = off % ld;
+                            if (row >= K || c0 >= R) fail("rc8 dword holds no element", off, row, c0, R);
+                            if (col < R && k < kend && off != (int64_t)k * ld + col)
+                                fail("rc8 wrong dword", off, col, k, 0);
+                            // the dword's bytes, masked to zero for k >= kend
+                            v[kk] = 0;
+                            for (int e = 0; e < 4; ++e)
+                                v[kk] |= (uint32_t)(k < kend ? code8(off + e) : 0) << (8 * e);
+                        }
+                        // the transposed chunk of each of the 4 rows
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = col + e;
+                            if (r >= R) continue;
+                            for (int d = 0; d < 4; ++d) {
+                                const uint32_t w = rc8_gather(v[4 * d], v[4 * d + 1], v[4 * d + 2],
+                                                              v[4 * d + 3], e);
+                                for (int q = 0; q < 4; ++q) {
+                                    const int k = k0 + kg * 16 + 4 * d + q;
+                                    const uint8_t want = k < kend ? code8((int64_t)k * ld + r) : 0;
+                                    if (((w >> (8 * q)) & 0xffu) != want)
+                                        fail("rc8 transposed byte", r, k, (w >> (8 * q)) & 0xffu, want);
+                                }
+                            }
+                        }
+                    }
+        }
+}
+
 // --------------------------------------------------------- LDS-DMA path
 // One operand tile of ROWS x BK 16-bit values through the DMA kernel's data
 // path, simulated: the value of X(r, k) is a unique code; the DMA mapping
@@ -204,6 +279,8 @@ int main() {
         for (const auto &t : tiles8) {
             const int kps = ((s.kps + t[1] - 1) / t[1]) * t[1];
             check_kc(t[0], t[1], t[2], 1, s.R, s.K, (s.ld + 15) / 16 * 16, kps);
+            check_rc8(t[0], t[1], t[2], s.R, s.K, (s.R + 15) / 16 * 16, kps);
+            check_rc8(t[0], t[1], t[2], s.R, s.K, (s.R + 15) / 16 * 16 + 16, kps);
         }
     }
     // R-contiguous B of the HGEMM workload exactly: 4001 columns, ldb 4008

@@ -48,6 +48,26 @@ def test_every_fp8_entry_format_layout(cid, fmt, la, lb):
 
 
 @pytest.mark.parametrize("cid", sorted(F8_ENTRY_TILE))
+@pytest.mark.parametrize("fmt", [FP8_E4M3, FP8_E5M2])
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR),
+                                   (COL_MAJOR, ROW_MAJOR)])
+def test_m_or_n_contiguous_operands_on_the_vector_path(cid, fmt, la, lb):
+    """16-byte aligned leading dimensions: row-major B and column-major A take
+    the transposing 8-bit vector loads; a ragged and a whole last K-tile."""
+    M, N, K0 = _shape(cid)
+    for K in (K0, 512):
+        # whole 16-byte lines, one line past the extent
+        lda = ((K if la == ROW_MAJOR else M) + 15) // 16 * 16 + 16
+        ldb = ((N if lb == ROW_MAJOR else K) + 15) // 16 * 16 + 16
+        for values, exact in (("int", True), ("uniform", False)):
+            prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, in_dtype=fmt, values=values,
+                                  c_values="normal" if values == "uniform" else "int",
+                                  lda=lda, ldb=ldb, ldd=N + 3, seed=9500 + cid + 10 * fmt)
+            _check(prob, exact, cid, "fp8 cfg%d fmt%d A%d B%d K%d %s vector" % (
+                cid, fmt, la, lb, K, values))
+
+
+@pytest.mark.parametrize("cid", sorted(F8_ENTRY_TILE))
 def test_fp8_output_modes(cid):
     M, N, K = _shape(cid)
     modes = [dict(out_dtype=F16, c_values="uniform", ldd=N + 3, satf=1),

@@ -62,6 +62,29 @@ def test_every_int8_entry_and_layout(cid, la, lb):
     _check(prob, cid, "i8 cfg%d A%d B%d" % (cid, la, lb))
 
 
+def _ld16(x):
+    """A leading dimension of whole 16-byte lines, one line past the extent."""
+    return (x + 15) // 16 * 16 + 16
+
+
+@pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR),
+                                   (COL_MAJOR, ROW_MAJOR)])
+@pytest.mark.parametrize("ragged", [True, False])
+def test_m_or_n_contiguous_operands_on_the_vector_path(cid, la, lb, ragged):
+    """16-byte aligned leading dimensions: row-major B and column-major A take
+    the transposing 8-bit vector loads (dword loads along M or N, transposed
+    in registers), with edge rows clamped, a ragged last K-tile masked, and
+    the padding lines poisoned."""
+    M, N, K = _shape(cid)
+    K = K if ragged else 512  # 512: a whole number of K-tiles of every entry
+    lda = _ld16(K if la == ROW_MAJOR else M)
+    ldb = _ld16(N if lb == ROW_MAJOR else K)
+    prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="full", c_values="big",
+                               lda=lda, ldb=ldb, ldd=N + 3, seed=8050 + cid + 3 * la + lb)
+    _check(prob, cid, "i8 cfg%d A%d B%d K%d vector" % (cid, la, lb, K))
+
+
 @pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
 def test_satf_clamps_and_in_place(cid):
     M, N, K = _shape(cid)
