@@ -155,10 +155,14 @@ int select_config(int64_t M, int64_t N, int64_t K, int klass, int cus) {
 // 16x16x32 MFMA (measured 6-8% faster at 4096^3: that MFMA sustains a higher
 // clock under the power limit); an N- or M-contiguous operand would need
 // transposed LDS reads, which cost more than the register-staged transpose
-// of the eight-wave tile.
+// of the eight-wave tile.  The large fp8 tile (four waves, 512 registers)
+// spills inside its K loop when an operand is M- or N-contiguous (the
+// transposing loads), so those take the 128x128 fp8 tile: 4096^3 with
+// row-major B 289 -> 152 us.
 int refine_large(int id, bool aligned, int layoutA, int layoutB) {
-    if (id == CFG_LARGE8 && aligned && layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR)
-        return CFG_LARGE_DMA16;
+    const bool kc = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
+    if (id == CFG_LARGE8 && aligned && kc) return CFG_LARGE_DMA16;
+    if (id == CFG_F8_LARGE && aligned && !kc) return CFG_F8_MEDIUM;
     return id;
 }
 
