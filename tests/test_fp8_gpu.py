@@ -55,7 +55,7 @@ def test_m_or_n_contiguous_operands_on_the_vector_path(cid, fmt, la, lb):
     """16-byte aligned leading dimensions: row-major B and column-major A take
     the transposing 8-bit vector loads; a ragged and a whole last K-tile."""
     M, N, K0 = _shape(cid)
-    for K in (K0, 512):
+    for K in (K0 + 3, 512):  # a last K-tile ending inside a 16-row block; whole K-tiles
         # whole 16-byte lines, one line past the extent
         lda = ((K if la == ROW_MAJOR else M) + 15) // 16 * 16 + 16
         ldb = ((N if lb == ROW_MAJOR else K) + 15) // 16 * 16 + 16

@@ -77,7 +77,9 @@ def test_m_or_n_contiguous_operands_on_the_vector_path(cid, la, lb, ragged):
     in registers), with edge rows clamped, a ragged last K-tile masked, and
     the padding lines poisoned."""
     M, N, K = _shape(cid)
-    K = K if ragged else 512  # 512: a whole number of K-tiles of every entry
+    # K + 3: a last K-tile that ends inside a 16-row block of the transposing
+    # loader; 512: a whole number of K-tiles of every entry
+    K = K + 3 if ragged else 512
     lda = _ld16(K if la == ROW_MAJOR else M)
     ldb = _ld16(N if lb == ROW_MAJOR else K)
     prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="full", c_values="big",
