@@ -84,17 +84,21 @@ const Entry kTable[] = {
     {"tiny_32x32x64_w1x1_mfma32x32x16", CfgTiny::BM, CfgTiny::BN, CfgTiny::BK, 0, 0, launch_tiny},
     {"large_dma_256x256x64_w2x2_mfma16x16x32", CfgLargeDma16::BM, CfgLargeDma16::BN,
      CfgLargeDma16::BK, 0, 0, launch_large_dma16},
+    {"large_dma8_256x256x64_w2x4_mfma16x16x32", CfgLargeDma8_16::BM, CfgLargeDma8_16::BN,
+     CfgLargeDma8_16::BK, 0, 0, launch_large_dma8_16},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
 enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
        CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8,
        CFG_F8_LARGE = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12,
-       CFG_LARGE_DMA = 13, CFG_TINY = 14, CFG_LARGE_DMA16 = 15 };
+       CFG_LARGE_DMA = 13, CFG_TINY = 14, CFG_LARGE_DMA16 = 15, CFG_LARGE_DMA8_16 = 16 };
 
 // Entries whose kernels load operands straight into LDS: 16-byte aligned
 // operands only (vec_ok); others run the entry of the same tile shape
 // with register-staged loads.
-bool needs_vec(int id) { return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16; }
+bool needs_vec(int id) {
+    return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16 || id == CFG_LARGE_DMA8_16;
+}
 
 
 // Compute units and XCDs of the current device, read once per device from

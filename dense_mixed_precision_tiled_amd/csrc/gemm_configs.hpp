@@ -31,6 +31,13 @@ using CfgSkinny = TileCfg<16, 128, 128, 1, 4, 16>;
 using CfgLargeDma = TileCfg<256, 256, 64, 2, 2, 32>;
 // The same with the 16x16x32 MFMA (8x8 tiles of 16x16 per wave).
 using CfgLargeDma16 = TileCfg<256, 256, 64, 2, 2, 16>;
+// The LDS-DMA K loop with eight waves of 128x64 (two per SIMD; 128
+// accumulators in AGPRs) and the 16x16x32 MFMA.  With two waves per SIMD
+// the transposed LDS reads of an N- or M-contiguous operand keep up, so both
+// operands arrive by DMA in every layout.  On par with the eight-wave
+// register-staged tile at 4096^3 and slightly ahead with K-contiguous
+// operands; an autotuning candidate.
+using CfgLargeDma8_16 = TileCfg<256, 256, 64, 2, 4, 16>;
 
 // int8 entries: the same tiles in bytes (BK = 128 int8 values per LDS row of
 // 128 bytes), v_mfma_i32_32x32x32_i8 / v_mfma_i32_16x16x64_i8.
@@ -70,6 +77,7 @@ LIBGEMM_DECLARE_LAUNCH(skinny)
 LIBGEMM_DECLARE_LAUNCH(large_dma)
 LIBGEMM_DECLARE_LAUNCH(tiny)
 LIBGEMM_DECLARE_LAUNCH(large_dma16)
+LIBGEMM_DECLARE_LAUNCH(large_dma8_16)
 #undef LIBGEMM_DECLARE_LAUNCH
 
 // one translation unit per int8 entry: kernels_<entry>_i8.hip (the bf flag of

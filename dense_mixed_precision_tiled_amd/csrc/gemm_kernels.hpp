@@ -1277,11 +1277,13 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     constexpr int KCH = CF::KSTEP * 2 / 16;       // 16-byte chunks per step (KC reads)
     static_assert(CF::ES == 2 && CF::FC == 1, "16-bit operands");
     static_assert(BK == 64, "LDS rows of 128 bytes (KC layout)");
-    // B_REG (row-major B with row-major A): B is loaded into registers and
-    // transposed on its way to LDS by LoaderRC, so LDS holds it K-contiguous
-    // like A; a transposed LDS read of B costs more than that register
-    // transpose (measured).  Column-major A keeps the transposed reads.
-    constexpr bool B_REG = A_KC && !B_KC;
+    // B_REG (row-major B with row-major A, one wave per SIMD): B is loaded
+    // into registers and transposed on its way to LDS by LoaderRC, so LDS
+    // holds it K-contiguous like A; with one wave per SIMD a transposed LDS
+    // read of B costs more than that register transpose (measured).  With
+    // two waves per SIMD, and with column-major A, B takes the transposed
+    // reads.
+    constexpr bool B_REG = A_KC && !B_KC && NWAVES == 4;
     constexpr bool B_KCL = B_KC || B_REG;  // B's LDS tile is K-contiguous
     using DA = DmaOperand<BM, BK, NWAVES, MF, A_KC, RAGGED>;
     using DB = DmaOperand<BN, BK, NWAVES, MF, B_KCL, RAGGED>;

@@ -286,10 +286,11 @@ int main() {
     // R-contiguous B of the HGEMM workload exactly: 4001 columns, ldb 4008
     check_rc(256, 64, 512, 4001, 4104, 4008, 4160);
     check_rc(256, 64, 256, 4001, 4104, 4008, 4160);
-    // the DMA kernel's tiles: 256 rows, BK 64, 4 waves, both MFMA shapes,
-    // both storage orders
-    for (int mf : {32, 16})
-        for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, 4);
+    // the DMA kernels' tiles: 256 rows, BK 64, 4 or 8 waves, both MFMA
+    // shapes, both storage orders
+    for (int nw : {4, 8})
+        for (int mf : {32, 16})
+            for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, nw);
     printf("checked %ld chunk reads, %ld failures\n", g_checked, g_fail);
     return g_fail ? 1 : 0;
 }

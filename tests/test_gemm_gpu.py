@@ -114,11 +114,11 @@ def test_multi_round_ragged_row_order_raster(values, exact):
 
 # tile-table entries: id -> block tile edge (None: the skinny split-K entry);
 # test_config_ids_match_table checks this against the library's table
-ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256, 13: 256, 14: 32, 15: 256}
+ENTRY_TILE = {0: 256, 1: 128, 2: 64, 3: None, 4: 256, 13: 256, 14: 32, 15: 256, 16: 256}
 # entries whose kernels load 16-byte aligned operands only (LDS DMA): their
 # sweeps use leading dimensions rounded up to 8 elements (still ragged M, N
 # and K, padding poisoned with NaN)
-VEC_ONLY = {13, 15}
+VEC_ONLY = {13, 15, 16}
 
 
 def _align(cid):
