@@ -129,10 +129,18 @@ hipError_t launch_one(const Params &p, dim3 grid, hipStream_t s) {
 template <class CF, int IT, bool AKC, bool BKC>
 hipError_t launch_dma_one(const Params &p, dim3 grid, hipStream_t s) {
     if (!p.vec_ok) return hipErrorInvalidValue;
-    const bool ragged = (p.K % CF::BK) != 0 || (p.k_per_split % CF::BK) != 0;
+    // Four-wave tiles with row-major A and B (B staged through registers)
+    // run the RAGGED kernel for every K (its last-tile handling is a uniform
+    // branch that whole K-tiles skip): its register allocation keeps the K
+    // loop free of AGPR shuffles, while the other one moved ~100 values
+    // through AGPRs per K-tile (4096^3: 163.5 -> 146-158 us).
+    constexpr bool always = CF::WAVES_M * CF::WAVES_N == 4 && AKC && !BKC;
+    const bool ragged = always || (p.K % CF::BK) != 0 || (p.k_per_split % CF::BK) != 0;
     const dim3 block(CF::THREADS);
     if (ragged) return launch_params(gemm_dma_kernel<CF, IT, AKC, BKC, true>, grid, block, p, s);
-    return launch_params(gemm_dma_kernel<CF, IT, AKC, BKC, false>, grid, block, p, s);
+    if constexpr (!always)
+        return launch_params(gemm_dma_kernel<CF, IT, AKC, BKC, false>, grid, block, p, s);
+    return hipErrorInvalidValue;  // not reached
 }
 
 template <class CF, int IT>
