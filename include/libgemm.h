@@ -192,11 +192,12 @@ const char *gemm_status_string(int status);
  * gemm_config_name: static text naming entry `config_id` (NULL if out of range).
  * gemm_select_config: the entry gemm_run would use for this problem with
  *                16-byte aligned operand lines, or a negative gemm_status_t
- *                if the arguments are invalid.  (Entries whose kernels load
- *                operands straight into LDS take aligned operands only; for
- *                others gemm_run runs the register-staged entry of the same
- *                tile shape, and gemm_run_config with such an entry returns
- *                GEMM_ERR_INVALID_CONFIG.)
+ *                if the arguments are invalid.  Entries whose kernels load
+ *                operands straight into LDS ("large_dma...") accept only
+ *                16-byte aligned operand lines: with other operands gemm_run
+ *                runs the register-staged 256x256 entry instead, and
+ *                gemm_run_config forced to such an entry returns
+ *                GEMM_ERR_INVALID_CONFIG.
  */
 int gemm_num_configs(void);
 const char *gemm_config_name(int config_id);
