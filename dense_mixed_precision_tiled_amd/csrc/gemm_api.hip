@@ -40,6 +40,20 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(Params p) {
     }
 }
 
+// Copy `rows` lines of `cols` elements from lines `ld_src` apart to lines
+// `ld_dst` apart (the operand repack of unaligned calls; the destination's
+// padding elements are left as they are: no stored output reads them).
+template <typename T>
+__global__ void __launch_bounds__(256) repack_lines_kernel(const T *src, int64_t ld_src, T *dst,
+                                                           int64_t ld_dst, int64_t rows,
+                                                           int64_t cols) {
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const T *s = src + r * ld_src;
+        T *d = dst + r * ld_dst;
+        for (int64_t c = threadIdx.x; c < cols; c += 256) d[c] = s[c];
+    }
+}
+
 }  // namespace libgemm
 
 namespace {
@@ -261,6 +275,48 @@ hipError_t scratch_address(float **out) {
 // Where run() takes the split-K workspace from.
 enum WorkspaceMode { WS_LIBRARY = 0, WS_STATIC_SCRATCH = 1 };
 
+// The copy of one operand into the workspace with lines of whole 16-byte
+// units (bytes == 0: no copy).  outer lines of inner elements of isz bytes.
+struct Repack {
+    int64_t outer = 0, inner = 0, ld = 0;  // ld: the copy's leading dimension
+    size_t bytes = 0;                      // workspace bytes (256-byte multiple)
+    int64_t rng = 0;                       // the copy's extent, rounded up to 16 bytes
+};
+
+Repack plan_repack(const void *X, int64_t ld, int64_t outer, int64_t inner, int isz) {
+    Repack r;
+    if ((uintptr_t)X % 16 == 0 && (ld * isz) % 16 == 0) return r;  // already aligned
+    const int64_t per = 16 / isz;  // elements per 16 bytes
+    r.outer = outer;
+    r.inner = inner;
+    r.ld = (inner + per - 1) / per * per;
+    r.rng = ((outer - 1) * r.ld + inner) * isz;
+    r.rng = (r.rng + 15) & ~(int64_t)15;
+    r.bytes = ((size_t)(outer * r.ld * isz) + 255) & ~(size_t)255;
+    return r;
+}
+
+hipError_t launch_repack(const void *src, int64_t ld_src, void *dst, const Repack &r, int isz,
+                         hipStream_t s) {
+    const int cus = topology().cus;
+    const int64_t blocks = r.outer < 8 * (int64_t)cus ? r.outer : 8 * (int64_t)cus;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (isz == 2) {
+        const uint16_t *sp = static_cast<const uint16_t *>(src);
+        uint16_t *dp = static_cast<uint16_t *>(dst);
+        int64_t lds = ld_src, ldd = r.ld, rows = r.outer, cols = r.inner;
+        void *args[] = {&sp, &lds, &dp, &ldd, &rows, &cols};
+        return hipLaunchKernel(reinterpret_cast<const void *>(repack_lines_kernel<uint16_t>), grid,
+                               block, args, 0, s);
+    }
+    const uint8_t *sp = static_cast<const uint8_t *>(src);
+    uint8_t *dp = static_cast<uint8_t *>(dst);
+    int64_t lds = ld_src, ldd = r.ld, rows = r.outer, cols = r.inner;
+    void *args[] = {&sp, &lds, &dp, &ldd, &rows, &cols};
+    return hipLaunchKernel(reinterpret_cast<const void *>(repack_lines_kernel<uint8_t>), grid,
+                           block, args, 0, s);
+}
+
 int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
         int layoutA, const void *B, int64_t ldb, int layoutB, const void *C, int64_t ldc,
         void *D, int64_t ldd, int in_dtype, int acc_dtype, int out_dtype, int satf,
@@ -340,11 +396,35 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const int64_t b_ext =
         (layoutB == GEMM_ROW_MAJOR ? (K - 1) * ldb + N : (N - 1) * ldb + K) * isz;
     const int64_t a_rng = (a_ext + 15) & ~(int64_t)15, b_rng = (b_ext + 15) & ~(int64_t)15;
+    int64_t a_rng_used = a_rng, b_rng_used = b_rng;
     p.vec_ok = K > 0 && ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) &&
                ((lda * isz) % 16 == 0) && ((ldb * isz) % 16 == 0) &&
                a_rng < ((int64_t)1 << 32) - 16 && b_rng < ((int64_t)1 << 32) - 16;
-    p.a_bytes = p.vec_ok ? (uint32_t)a_rng : 0u;
-    p.b_bytes = p.vec_ok ? (uint32_t)b_rng : 0u;
+    // Large calls whose operands miss the vector path only by alignment copy
+    // the offending operand(s) into the library workspace with lines of
+    // whole 16-byte units first (a line copy costs far less than the
+    // element-wise loads: 4096^3 fp16 with lda = 4097 ~600 us unpacked).  The
+    // call without allocation (gemm_run_noalloc) keeps the element path.
+    Repack rp_a, rp_b;
+    if (!p.vec_ok && ws_mode == WS_LIBRARY && K > 0 && M * N * K >= ((int64_t)1 << 30)) {
+        rp_a = plan_repack(A, lda, layoutA == GEMM_ROW_MAJOR ? M : K,
+                           layoutA == GEMM_ROW_MAJOR ? K : M, isz);
+        rp_b = plan_repack(B, ldb, layoutB == GEMM_ROW_MAJOR ? K : N,
+                           layoutB == GEMM_ROW_MAJOR ? N : K, isz);
+        const int64_t a2 = rp_a.bytes ? rp_a.rng : a_rng, b2 = rp_b.bytes ? rp_b.rng : b_rng;
+        const bool a_al = rp_a.bytes || (((uintptr_t)A % 16 == 0) && ((lda * isz) % 16 == 0));
+        const bool b_al = rp_b.bytes || (((uintptr_t)B % 16 == 0) && ((ldb * isz) % 16 == 0));
+        if (a_al && b_al && a2 < ((int64_t)1 << 32) - 16 && b2 < ((int64_t)1 << 32) - 16) {
+            p.vec_ok = 1;
+            a_rng_used = a2;
+            b_rng_used = b2;
+        } else {
+            rp_a = Repack{};
+            rp_b = Repack{};
+        }
+    }
+    p.a_bytes = p.vec_ok ? (uint32_t)a_rng_used : 0u;
+    p.b_bytes = p.vec_ok ? (uint32_t)b_rng_used : 0u;
     if (needs_vec(id) && !p.vec_ok) {
         // a forced entry that cannot run these operands is an error; the
         // dispatcher's choice falls back to the register-staged large tile
@@ -388,19 +468,44 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     dim3 grid((unsigned)tiles, 1, (unsigned)splits);
     // the launcher's variant flag: bf16 among the 16-bit inputs, E5M2 among fp8
     const int variant = (in_dtype == GEMM_BF16 || in_dtype == GEMM_FP8_E5M2) ? 1 : 0;
+    const bool repack = rp_a.bytes || rp_b.bytes;
+    if (splits == 1 && !repack)
+        return E.launch(p, variant, akc, bkc, grid, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+
+    // Workspace: repacked operands, then the split-K slices.  The lock is
+    // held until every launch of the call is enqueued, so the call's
+    // launches stay in one piece in the stream's order.
+    const size_t ws_split = splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+    const size_t ws_bytes = rp_a.bytes + rp_b.bytes + ws_split;
+    std::unique_lock<std::mutex> ws_lock;
+    char *ws = nullptr;
+    if (ws_mode == WS_STATIC_SCRATCH) {
+        if (ws_bytes > kScratchBytes) return GEMM_ERR_SCRATCH_TOO_SMALL;
+        float *w = nullptr;
+        if (scratch_address(&w) != hipSuccess) return GEMM_ERR_HIP;
+        ws = reinterpret_cast<char *>(w);
+    } else {
+        ws_lock = std::unique_lock<std::mutex>(g_ws_mutex);
+        float *w = nullptr;
+        if (workspace_locked(stream, ws_bytes, &w) != hipSuccess) return GEMM_ERR_HIP;
+        ws = reinterpret_cast<char *>(w);
+    }
+    if (rp_a.bytes) {
+        if (launch_repack(A, lda, ws, rp_a, isz, stream) != hipSuccess) return GEMM_ERR_HIP;
+        p.A = reinterpret_cast<const uint16_t *>(ws);
+        p.lda = rp_a.ld;
+    }
+    if (rp_b.bytes) {
+        char *dst = ws + rp_a.bytes;
+        if (launch_repack(B, ldb, dst, rp_b, isz, stream) != hipSuccess) return GEMM_ERR_HIP;
+        p.B = reinterpret_cast<const uint16_t *>(dst);
+        p.ldb = rp_b.ld;
+    }
+    p.ws = reinterpret_cast<float *>(ws + rp_a.bytes + rp_b.bytes);
     if (splits == 1)
         return E.launch(p, variant, akc, bkc, grid, stream) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 
     // split-K: slice kernel into the workspace, then the reduction into D
-    const size_t ws_bytes = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
-    std::unique_lock<std::mutex> ws_lock;
-    if (ws_mode == WS_STATIC_SCRATCH) {
-        if (ws_bytes > kScratchBytes) return GEMM_ERR_SCRATCH_TOO_SMALL;
-        if (scratch_address(&p.ws) != hipSuccess) return GEMM_ERR_HIP;
-    } else {
-        ws_lock = std::unique_lock<std::mutex>(g_ws_mutex);
-        if (workspace_locked(stream, ws_bytes, &p.ws) != hipSuccess) return GEMM_ERR_HIP;
-    }
     if (E.launch(p, variant, akc, bkc, grid, stream) != hipSuccess) return GEMM_ERR_HIP;
     const int64_t total = M * N;
     int64_t blocks = cdiv(total, 256);

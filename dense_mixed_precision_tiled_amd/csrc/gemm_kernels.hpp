@@ -523,9 +523,10 @@ struct LoaderRC8 {
                 if (k0 + kg[j] * 16 + kk >= kend) v[j][kk] = 0u;
     }
 
-    // the idx-th LDS store: block idx / 4, row 4rg + idx % 4
+    // the idx-th LDS store: block idx / 4, row 4rg + idx % 4 (the thread's
+    // blocks are fixed at init; tid keeps the loaders' common signature)
     template <int idx>
-    __device__ __forceinline__ void store_one(u32x4 *lds, int tid) const {
+    __device__ __forceinline__ void store_one(u32x4 *lds, int /*tid*/) const {
         constexpr int j = idx / 4, e = idx % 4;
         u32x4 w;
 #pragma unroll
@@ -940,7 +941,7 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
                                        typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
                                        u32x4 *sA, u32x4 *sB, int tid) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK, CH = CF::CH;
-    constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN, THREADS = CF::THREADS;
+    constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
     constexpr int KS = BK / CF::KSTEP;           // MFMA steps per K-tile
     constexpr int KCH = CF::KSTEP * CF::ES / 16;  // 16-byte LDS chunks per MFMA step
     static_assert(KS % 2 == 0 && KS >= 2, "fragment slots alternate across K-tiles; the"

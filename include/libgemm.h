@@ -113,27 +113,31 @@ typedef enum {
  *                on it; the call does not wait for it.
  *
  * Ownership: every pointer is owned by the caller and must stay valid until
- * the stream reaches the enqueued work.  Problems split along K (M <= 16)
- * use a device workspace the library owns for the partial sums: one per
- * (device, stream) pair, allocated with hipMalloc on first need and grown
- * on demand.  A call holds the workspace's lock from taking the buffer until
- * both of its launches are enqueued, so calls from several host threads on
- * one stream are enqueued one after the other; an outgrown buffer is never
- * freed (work enqueued earlier may still use it).  Workspaces are kept until
- * the process exits.
+ * the stream reaches the enqueued work.  Problems split along K (M <= 16),
+ * and large calls (M*N*K >= 2^30) whose A or B misses the vector loads only
+ * by alignment (that operand is first copied there with 16-byte lines), use
+ * a device workspace the library owns: one per (device, stream) pair,
+ * allocated with hipMalloc on first need and grown on demand.  A call holds
+ * the workspace's lock from taking the buffer until all of its launches are
+ * enqueued, so calls from several host threads on one stream are enqueued
+ * one after the other; an outgrown buffer is never freed (work enqueued
+ * earlier may still use it).  Workspaces are kept until the process exits.
  *
  * Errors: argument errors are detected on the host before anything is
  * enqueued, and nothing is written.  GEMM_ERR_HIP reports a launch or
  * allocation failure (the launch's own status, not an earlier error); D is
- * then not written, except that a split-K call whose reduction launch fails
- * has already enqueued its slice kernel, which writes only the workspace.
+ * then not written, except that a call whose later launch fails has already
+ * enqueued the earlier ones (an operand copy, a split-K slice kernel), which
+ * write only the workspace.
  * Faults inside the kernels surface at the next synchronisation of the
  * stream.
  *
  * Speed: vector loads are used where A and B base pointers are 16-byte
  * aligned and lda, ldb are multiples of 16 bytes (the pages' ldm rule), in
  * every layout (operands contiguous along M or N are transposed on the way
- * to LDS); anything else runs correct element-wise loads.  C and D
+ * to LDS); large calls with other operands copy them into the workspace
+ * with 16-byte lines first (see Ownership), and the rest run correct
+ * element-wise loads.  C and D
  * are read and written four elements at a time where their base pointers
  * are aligned to four elements, ldc and ldd are multiples of 4 and C is
  * row-major (and, for gemm_run_ex, a per-column bias is 16-byte aligned);
@@ -156,7 +160,10 @@ int gemm_run(int64_t M, int64_t N, int64_t K,
  * gemm_run without any device allocation, for callers that cannot allocate:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments, validation and results as gemm_run (the same
- * kernels, bit-identical D).  Where gemm_run would take its split-K partial
+ * kernels, bit-identical D), except for large calls whose operands gemm_run
+ * would copy into its workspace for alignment: this call runs those with
+ * element-wise loads instead (the same results to the stated tolerances;
+ * slower).  Where gemm_run would take its split-K partial
  * sums from a workspace it allocates (M <= 16), this call uses a scratch
  * array of fixed size compiled into the library: 32 MiB of device memory per
  * GPU the library runs on, held until the process ends.  Problems whose

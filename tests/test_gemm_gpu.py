@@ -234,6 +234,23 @@ def test_large_unaligned_falls_back_to_staged_loads(values, exact):
     _full_check(prob, exact, label="large unaligned %s" % values)
 
 
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, ROW_MAJOR), (ROW_MAJOR, COL_MAJOR),
+                                   (COL_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR)])
+def test_large_unaligned_operands_are_repacked(la, lb):
+    """M*N*K >= 2^30 with leading dimensions that miss 16-byte lines: the
+    library copies the operands into its workspace with aligned lines and
+    runs the vector path (padding of the originals poisoned with NaN; ragged
+    M, N and K; fp32 C).  Whole output against the oracle."""
+    M, N, K = 1030, 1031, 1029
+    lda = (K if la == ROW_MAJOR else M) + 3
+    ldb = (N if lb == ROW_MAJOR else K) + 1
+    for values, exact in (("int", True), ("uniform", False)):
+        prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, values=values, lda=lda, ldb=ldb,
+                              c_values="int" if exact else "normal", ldd=N + 2,
+                              seed=3150 + 2 * la + lb)
+        _full_check(prob, exact, label="repacked A%d B%d %s" % (la, lb, values))
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 7, 3), (5, 1, 9), (17, 33, 8), (31, 15, 9),
                                    (64, 64, 64), (65, 63, 65), (16, 16, 1), (33, 257, 31),
                                    (100, 100, 0)])

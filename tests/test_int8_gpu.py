@@ -123,6 +123,15 @@ def test_unaligned_leading_dims_take_the_element_path():
     _check(prob, None, "i8 unaligned")
 
 
+def test_large_unaligned_operands_are_repacked():
+    """M*N*K >= 2^30 with unaligned leading dimensions: the operands are
+    copied into the workspace with 16-byte lines, then the vector path."""
+    prob = W.make_int8_problem(1030, 1031, 1029, layoutB=ROW_MAJOR, lda=1029 + 3,
+                               ldb=1031 + 5, values="full", c_values="big", ldd=1033,
+                               seed=8310)
+    _check(prob, None, "i8 repacked")
+
+
 def test_wraps_modulo_2_32_beyond_2_17_products():
     """K = 140000 products of magnitude up to 2^14: sums leave the int32 range
     and wrap, exactly as the oracle's modular reduction of the exact sum."""
