@@ -133,4 +133,35 @@ LIBGEMM_HD inline int tr_read_offset(int lane, int mf, int ks, int h, int rb, in
     return krow * rowbytes + (((row / 8) ^ swz_rc(krow, mf)) * 16) + (row % 8) * 2;
 }
 
+// Output tile of workgroup w.  The device hands workgroups to its xcds XCDs
+// in turn (w % xcds), so the linear tile index t gives each XCD one
+// contiguous run of tiles and the XCD's concurrent workgroups run
+// neighbouring tiles, which share operand panels in that XCD's L2.  Tiles
+// are numbered in raster groups of group_m tile-rows, column by column
+// inside a group (row order when group_m is 1).  With skew, group g starts
+// at column g * tiles_n / groups and wraps around: groups that run at the
+// same time on different XCDs then work on different column bands, so their
+// reads of B and their writes of D spread over the memory channels instead
+// of all XCDs streaming the same columns.  Every step is a bijection of
+// [0, tiles_m * tiles_n), so each tile is computed exactly once.
+LIBGEMM_HD inline void raster_tile(int w, int tiles_m, int tiles_n, int group_m, int xcds,
+                                   int skew, int &tm, int &tn) {
+    const int T = tiles_m * tiles_n;
+    const int xcd = w % xcds, local = w / xcds;
+    const int per = T / xcds, rem = T % xcds;
+    const int t = xcd * per + imin(xcd, rem) + local;
+    const int in_group = group_m * tiles_n;
+    const int g = t / in_group;
+    const int first_m = g * group_m;
+    const int gsize = imin(tiles_m - first_m, group_m);
+    const int t_in = t - g * in_group;
+    tm = first_m + t_in % gsize;
+    tn = t_in / gsize;
+    if (skew) {
+        const int groups = (tiles_m + group_m - 1) / group_m;
+        tn += g * tiles_n / groups;  // g * tiles_n <= tiles_m * tiles_n, an int
+        if (tn >= tiles_n) tn -= tiles_n;
+    }
+}
+
 }  // namespace libgemm

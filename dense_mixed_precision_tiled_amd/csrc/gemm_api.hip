@@ -443,11 +443,17 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     if (tiles > 0x7fffffff) return GEMM_ERR_INVALID_DIM;
     // Raster groups of 4 tile-rows per XCD keep the L2 fills low.  When each
-    // CU runs several 256x256 tiles with a short K loop, D's stores dominate
-    // and plain row order is faster: its concurrent tiles write D in wider
-    // column bands (16384^2 x 1024: 14% faster for fp16, 25% for int8 and
-    // fp8; at 8192^3 row order was 5% slower, at 4096^3 and 6144^3 on par).
-    p.group_m = (E.BM == 256 && tiles > topo.cus && K <= 2048) ? 1 : 4;
+    // CU runs several 256x256 tiles with a short K loop, D's stores and the B
+    // panels' refills share the memory system with the K loop: groups of 2
+    // tile-rows whose starting columns are staggered by group (skew) halve
+    // the B refills of row order and keep the XCDs on different column bands
+    // (16384^2 x 1024: 3-4% faster than row order for fp16, 5% for int8;
+    // unstaggered groups of 2 to 8 rows were 8-40% slower than row order,
+    // as every XCD then streams the same narrow column band).  At 8192^3 and
+    // at one tile per CU the stagger changed nothing measurable.
+    const bool short_multi = E.BM == 256 && tiles > topo.cus && K <= 2048;
+    p.group_m = short_multi ? 2 : 4;
+    p.skew = short_multi ? 1 : 0;
     p.xcds = topo.xcds;
 
     // K slices: enough workgroups for 4 per CU, each slice >= 8 K-tiles

@@ -89,7 +89,8 @@ struct Params {
     int cd_vec;      // C, D rows allow 4-element vector access (aligned base, ld % 4 == 0)
     uint32_t a_bytes, b_bytes;  // vector path: A, B extents rounded up to 16 bytes
     int tiles_m, tiles_n;
-    int group_m;     // tile-rows per raster group (see map_tile)
+    int group_m;     // tile-rows per raster group (see raster_tile)
+    int skew;        // raster groups start at staggered columns (see raster_tile)
     int xcds;        // XCDs the device hands workgroups to (round-robin)
     int splits;      // K slices (blockIdx.z); 1 = no split
     int k_per_split; // multiple of BK
@@ -893,25 +894,10 @@ __device__ __forceinline__ void finish4(const Params &p, int i, int j, f32x4 v) 
 }
 
 // ------------------------------------------------------------ tile mapping
-// Workgroups are handed to the device's p.xcds XCDs round-robin (workgroup w
-// runs on XCD w % xcds).  Renumber them so each XCD receives a contiguous
-// range of tiles (a bijection for any tile count), then walk tiles in groups
-// of p.group_m tile-rows, so the tiles that share A row-panels and B
-// column-panels run on the same XCD's L2.
+// XCD-aware renumbering and grouped raster of gemm_address.hpp (raster_tile),
+// with the group height and skew the host chose for the call.
 __device__ __forceinline__ void map_tile(const Params &p, int w, int &tm, int &tn) {
-    const int GROUP_M = p.group_m;
-    const int T = p.tiles_m * p.tiles_n;
-    const int nx = p.xcds;
-    const int xcd = w % nx, local = w / nx;
-    const int per = T / nx, rem = T % nx;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int in_group = GROUP_M * p.tiles_n;
-    const int g = t / in_group;
-    const int first_m = g * GROUP_M;
-    const int gsize = (p.tiles_m - first_m) < GROUP_M ? (p.tiles_m - first_m) : GROUP_M;
-    const int t_in = t - g * in_group;
-    tm = first_m + t_in % gsize;
-    tn = t_in / gsize;
+    raster_tile(w, p.tiles_m, p.tiles_n, p.group_m, p.xcds, p.skew, tm, tn);
 }
 
 // ------------------------------------------------------------------ K loop

@@ -11,6 +11,7 @@
 #include <stdlib.h>
 
 #include <initializer_list>
+#include <vector>
 
 #include "gemm_address.hpp"
 
@@ -257,6 +258,24 @@ static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves) {
     free(filled);
 }
 
+// raster_tile must hit every tile of the grid exactly once.
+static void check_raster(int tiles_m, int tiles_n, int group_m, int xcds, int skew) {
+    const int T = tiles_m * tiles_n;
+    std::vector<int> hits((size_t)T, 0);
+    for (int w = 0; w < T; ++w) {
+        int tm = -1, tn = -1;
+        libgemm::raster_tile(w, tiles_m, tiles_n, group_m, xcds, skew, tm, tn);
+        ++g_checked;
+        if (tm < 0 || tm >= tiles_m || tn < 0 || tn >= tiles_n) {
+            fail("raster tile out of the grid", w, tm, tn, group_m);
+            continue;
+        }
+        ++hits[(size_t)tm * tiles_n + tn];
+    }
+    for (int i = 0; i < T; ++i)
+        if (hits[(size_t)i] != 1) fail("raster tile not hit once", i, hits[(size_t)i], tiles_m, tiles_n);
+}
+
 int main() {
     // (R, K, ld) problem sides: the HGEMM workload (A 3999 x 4104 lda 4104, B
     // row-major 4104 x 4001 ldb 4008), ragged small shapes, K below one tile,
@@ -291,6 +310,13 @@ int main() {
     for (int nw : {4, 8})
         for (int mf : {32, 16})
             for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, nw);
-    printf("checked %ld chunk reads, %ld failures\n", g_checked, g_fail);
+    // the raster: grids of one tile to several rounds per CU, ragged groups,
+    // every group height and XCD count the host uses, with and without skew
+    const int grids[][2] = {{1, 1}, {1, 7}, {7, 1}, {16, 16}, {64, 64}, {63, 65}, {5, 33}, {32, 32}, {3, 200}};
+    for (const auto &gd : grids)
+        for (int gm : {1, 2, 4, 8})
+            for (int nx : {1, 2, 8})
+                for (int sk : {0, 1}) check_raster(gd[0], gd[1], gm, nx, sk);
+    printf("checked %ld chunk reads and raster tiles, %ld failures\n", g_checked, g_fail);
     return g_fail ? 1 : 0;
 }

@@ -3,7 +3,10 @@ loaders compose their byte offsets from the functions of
 ``csrc/gemm_address.hpp``; ``address_check.cpp`` composes them the same way
 for every tile, thread, chunk and K-tile of a set of problems (the HGEMM
 workload's ragged K among them) and checks that every 16-byte chunk read lies
-inside the operand and holds one of its elements.  Built with g++ under
+inside the operand and holds one of its elements.  It also walks the
+workgroup-to-tile raster (``raster_tile``) over grids, group heights, XCD
+counts and the skewed column order, and checks that every tile is computed
+exactly once.  Built with g++ under
 AddressSanitizer and UndefinedBehaviorSanitizer."""
 import os
 import shutil

@@ -101,10 +101,11 @@ def test_skinny_16x16384x16384(values, exact):
 
 
 @pytest.mark.parametrize("values,exact", [("uniform", False), ("int", True)])
-def test_multi_round_ragged_row_order_raster(values, exact):
+def test_multi_round_ragged_skewed_raster(values, exact):
     """17 x 19 tiles of 256 (more than one per CU) with K <= 2048: the host
-    walks the tiles in plain row order instead of groups of 4 tile-rows.
-    Ragged M and N, fp32 C; the whole output."""
+    walks the tiles in groups of 2 tile-rows with staggered starting columns
+    (the last group holds one tile-row) instead of groups of 4.  Ragged M and
+    N, fp32 C; the whole output."""
     prob = W.make_problem(4100, 4610, 1000, values=values, c_values="normal" if values ==
                           "uniform" else "int", seed=20311, name="4100x4610x1000 +C")
     _whole_check(prob, exact)
