@@ -100,18 +100,33 @@ const Entry kTable[] = {
      CfgLargeDma16::BK, 0, 0, launch_large_dma16},
     {"large_dma8_256x256x64_w2x4_mfma16x16x32", CfgLargeDma8_16::BM, CfgLargeDma8_16::BN,
      CfgLargeDma8_16::BK, 0, 0, launch_large_dma8_16},
+    {"i8_large_dma8_256x256x128_w2x4_mfma32x32x32", CfgLargeDma8I8::BM, CfgLargeDma8I8::BN,
+     CfgLargeDma8I8::BK, 0, 1, launch_large_dma8_i8},
+    {"fp8_large_dma8_256x256x128_w2x4_mfma32x32x64", CfgLargeDma8F8::BM, CfgLargeDma8F8::BN,
+     CfgLargeDma8F8::BK, 0, 2, launch_large_dma8_fp8},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
 enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
        CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8,
        CFG_F8_LARGE = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12,
-       CFG_LARGE_DMA = 13, CFG_TINY = 14, CFG_LARGE_DMA16 = 15, CFG_LARGE_DMA8_16 = 16 };
+       CFG_LARGE_DMA = 13, CFG_TINY = 14, CFG_LARGE_DMA16 = 15, CFG_LARGE_DMA8_16 = 16,
+       CFG_I8_LARGE_DMA8 = 17, CFG_F8_LARGE_DMA8 = 18 };
 
 // Entries whose kernels load operands straight into LDS: 16-byte aligned
 // operands only (vec_ok); others run the entry of the same tile shape
 // with register-staged loads.
 bool needs_vec(int id) {
-    return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16 || id == CFG_LARGE_DMA8_16;
+    return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16 || id == CFG_LARGE_DMA8_16 ||
+           id == CFG_I8_LARGE_DMA8 || id == CFG_F8_LARGE_DMA8;
+}
+// The 8-bit LDS-DMA entries also need both operands K-contiguous (as the
+// kernels see them: row-major A, column-major B).
+bool needs_kc(int id) {
+    return id == CFG_I8_LARGE_DMA8 || id == CFG_F8_LARGE_DMA8;
+}
+// the register-staged large tile of each input class
+int class_large(int klass) {
+    return klass == 1 ? CFG_I8_LARGE8 : klass == 2 ? CFG_F8_LARGE : CFG_LARGE8;
 }
 
 
@@ -168,18 +183,24 @@ int select_config(int64_t M, int64_t N, int64_t K, int klass, int cus) {
     return e[4];
 }
 
-// The dispatcher's large 16-bit tile: with both operands K-contiguous (A
+// The dispatcher's large tiles.  16-bit: with both operands K-contiguous (A
 // row-major, B column-major) and 16-byte aligned, the LDS-DMA kernel with the
 // 16x16x32 MFMA (measured 6-8% faster at 4096^3: that MFMA sustains a higher
 // clock under the power limit); an N- or M-contiguous operand would need
 // transposed LDS reads, which cost more than the register-staged transpose
-// of the eight-wave tile.  The large fp8 tile (four waves, 512 registers)
-// spills inside its K loop when an operand is M- or N-contiguous (the
-// transposing loads), so those take the 128x128 fp8 tile: 4096^3 with
-// row-major B 289 -> 152 us.
-int refine_large(int id, bool aligned, int layoutA, int layoutB) {
+// of the eight-wave tile.  fp8: with K-contiguous aligned operands and whole
+// K-tiles, the eight-wave LDS-DMA tile (4096^3 ~6% faster than the four-wave
+// register-staged one; its ragged-K kernel spills a few registers in the K
+// loop, so a ragged K keeps the four-wave tile).  The four-wave fp8 tile
+// (512 registers) spills inside its K loop when an operand is M- or
+// N-contiguous (the transposing loads), so those take the 128x128 fp8 tile:
+// 4096^3 with row-major B 289 -> 152 us.  int8 keeps its eight-wave
+// register-staged tile: the LDS-DMA int8 entry measured on par with it.
+int refine_large(int id, bool aligned, int layoutA, int layoutB, int64_t K) {
     const bool kc = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
     if (id == CFG_LARGE8 && aligned && kc) return CFG_LARGE_DMA16;
+    if (id == CFG_F8_LARGE && aligned && kc && K % CfgLargeDma8F8::BK == 0)
+        return CFG_F8_LARGE_DMA8;
     if (id == CFG_F8_LARGE && aligned && !kc) return CFG_F8_MEDIUM;
     return id;
 }
@@ -425,13 +446,14 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     }
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng_used : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng_used : 0u;
-    if (needs_vec(id) && !p.vec_ok) {
+    const bool kc_ops = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
+    if ((needs_vec(id) && !p.vec_ok) || (needs_kc(id) && !kc_ops)) {
         // a forced entry that cannot run these operands is an error; the
         // dispatcher's choice falls back to the register-staged large tile
         if (config_id >= 0) return GEMM_ERR_INVALID_CONFIG;
-        id = CFG_LARGE8;
+        id = class_large(klass);
     }
-    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB);
+    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB, K);
     const Entry &E = kTable[id];
     const int osz = out_size(out_dtype);
     // register epilogue (vector C, D and bias access): aligned row-major C and D
@@ -719,7 +741,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
                             1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr, 0);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
     return refine_large(select_config(M, N, K, input_class(in_dtype), topology().cus), true,
-                        layoutA, layoutB);
+                        layoutA, layoutB, K);
 }
 
 }  // extern "C"

@@ -57,6 +57,14 @@ using CfgMediumF8 = TileCfg<128, 128, 128, 2, 2, 32, 1, 2>;
 using CfgSmallF8 = TileCfg<64, 64, 128, 2, 2, 32, 1, 2>;
 using CfgSkinnyF8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 2>;
 
+// The LDS-DMA K loop for 8-bit operands that are both K-contiguous (row-major
+// A, column-major B, 16-byte aligned rows): eight waves of 128x64 (two per
+// SIMD, 128 accumulators each), LDS rows of 128 bytes (BK = 128 values).  No
+// operand passes through registers on its way to LDS, which leaves room for
+// the fp8 MFMA's two-chunk fragments at two waves per SIMD.
+using CfgLargeDma8I8 = TileCfg<256, 256, 128, 2, 4, 32, 1>;
+using CfgLargeDma8F8 = TileCfg<256, 256, 128, 2, 4, 32, 1, 2>;
+
 typedef hipError_t (*launch_fn)(const Params &, int bf16, int a_kcontig, int b_kcontig,
                                 dim3 grid, hipStream_t stream);
 
@@ -86,6 +94,7 @@ hipError_t launch_large8_i8(const Params &, int, int, int, dim3, hipStream_t);
 hipError_t launch_medium_i8(const Params &, int, int, int, dim3, hipStream_t);
 hipError_t launch_small_i8(const Params &, int, int, int, dim3, hipStream_t);
 hipError_t launch_skinny_i8(const Params &, int, int, int, dim3, hipStream_t);
+hipError_t launch_large_dma8_i8(const Params &, int, int, int, dim3, hipStream_t);
 
 // fp8 entries, one translation unit per (entry, format): kernels_<entry>_f8.hip
 // (E4M3) and kernels_<entry>_bf8.hip (E5M2); the bf flag of launch_fn selects
@@ -102,6 +111,7 @@ LIBGEMM_DECLARE_LAUNCH_F8(large)
 LIBGEMM_DECLARE_LAUNCH_F8(medium)
 LIBGEMM_DECLARE_LAUNCH_F8(small)
 LIBGEMM_DECLARE_LAUNCH_F8(skinny)
+LIBGEMM_DECLARE_LAUNCH_F8(large_dma8)
 #undef LIBGEMM_DECLARE_LAUNCH_F8
 
 // Launch a kernel taking Params by value; the launch's own status is returned
@@ -145,11 +155,17 @@ hipError_t launch_dma_one(const Params &p, dim3 grid, hipStream_t s) {
 
 template <class CF, int IT>
 hipError_t launch_dma_layouts(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
-    if (akc)
-        return bkc ? launch_dma_one<CF, IT, true, true>(p, grid, s)
-                   : launch_dma_one<CF, IT, true, false>(p, grid, s);
-    return bkc ? launch_dma_one<CF, IT, false, true>(p, grid, s)
-               : launch_dma_one<CF, IT, false, false>(p, grid, s);
+    if constexpr (CF::ES == 1) {
+        // 8-bit operands: K-contiguous A and B only (the host sends no others)
+        if (!akc || !bkc) return hipErrorInvalidValue;
+        return launch_dma_one<CF, IT, true, true>(p, grid, s);
+    } else {
+        if (akc)
+            return bkc ? launch_dma_one<CF, IT, true, true>(p, grid, s)
+                       : launch_dma_one<CF, IT, true, false>(p, grid, s);
+        return bkc ? launch_dma_one<CF, IT, false, true>(p, grid, s)
+                   : launch_dma_one<CF, IT, false, false>(p, grid, s);
+    }
 }
 
 template <class CF, int IT>

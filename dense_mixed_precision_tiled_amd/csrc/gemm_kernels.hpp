@@ -1141,9 +1141,11 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
 // way to LDS, so there is no staging, no ds_write and no in-register
 // transpose.  Each operand keeps its storage order in LDS:
 //   K-contiguous (row-major A, column-major B): [rows][BK] in 16-byte chunks,
-//     read with ds_read_b128 (one chunk per lane and MFMA operand);
-//   R-contiguous (row-major B, column-major A): [BK][rows], read with the
-//     transposing ds_read_b64_tr_b16 (two per lane and MFMA operand).
+//     read with ds_read_b128 (one chunk per lane and MFMA operand, two for
+//     the fp8 MFMAs); 16-bit and 8-bit values alike (rows of 128 bytes);
+//   R-contiguous (row-major B, column-major A; 16-bit only): [BK][rows],
+//     read with the transposing ds_read_b64_tr_b16 (two per lane and MFMA
+//     operand).
 // The XOR swizzles (gemm_address.hpp) are applied on the global side: lane l
 // of a DMA instruction fills LDS chunk q0 + l, so it fetches the chunk that
 // belongs in that slot.
@@ -1184,15 +1186,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst
                                              (int)soff, 0, 0);
 }
 
-// One operand's DMA for the K loop: ROWS x BK tile of 16-bit values, KC or
-// R-contiguous storage, NWAVES waves sharing the tile's 1 KiB DMA blocks.
-template <int ROWS, int BK, int NWAVES, int MF, bool KC, bool CLAMPK>
+// One operand's DMA for the K loop: ROWS x BK tile of ES-byte values (16-bit,
+// or 8-bit when K-contiguous), KC or R-contiguous storage, NWAVES waves
+// sharing the tile's 1 KiB DMA blocks.
+template <int ROWS, int BK, int NWAVES, int MF, bool KC, bool CLAMPK, int ES = 2>
 struct DmaOperand {
-    static constexpr int BYTES = ROWS * BK * 2;
+    static constexpr int BYTES = ROWS * BK * ES;
     static constexpr int NI = BYTES / 1024 / NWAVES;  // DMA instructions per wave
     static_assert(BYTES % (1024 * NWAVES) == 0, "1 KiB DMA blocks per wave");
-    static constexpr int CH = BK / 8;      // KC: chunks per row
-    static constexpr int CHR = ROWS / 8;   // RC: chunks per k-row
+    static_assert(ES == 2 || KC, "8-bit operands: K-contiguous only");
+    static constexpr int EPC = 16 / ES;      // elements per 16-byte chunk
+    static constexpr int CH = BK * ES / 16;  // KC: chunks per row
+    static constexpr int CHR = ROWS / 8;     // RC: chunks per k-row
     static_assert(KC || ROWS >= 128, "the R-contiguous swizzle needs 16 chunks per k-row");
     uint32_t voff[NI];  // byte offset at k0 = 0 (CLAMPK: without the k part)
     int kpos[NI];       // CLAMPK: k position of the chunk (KC) or the k-row (RC)
@@ -1203,9 +1208,10 @@ struct DmaOperand {
             const int q = (wave * NI + i) * 64 + lane;
             int a, c;
             if constexpr (KC) {
-                dma_kc_source(q, CH, a, c);  // a = row, chunk c holds k = 8c..8c+7
-                kpos[i] = 8 * c;
-                voff[i] = (uint32_t)kc_chunk_offset(r0 + a, CLAMPK ? 0 : 8 * c, R, 1, ld, 2, false);
+                dma_kc_source(q, CH, a, c);  // a = row, chunk c holds k = EPC*c..
+                kpos[i] = EPC * c;
+                voff[i] =
+                    (uint32_t)kc_chunk_offset(r0 + a, CLAMPK ? 0 : EPC * c, R, 1, ld, ES, false);
             } else {
                 dma_rc_source(q, CHR, MF, a, c);  // a = k-row, rows 8c..8c+7
                 kpos[i] = a;
@@ -1222,9 +1228,9 @@ struct DmaOperand {
         char *dst = real ? lds + (wave * NI + i) * 1024 : sink;
         if constexpr (KC) {
             if constexpr (CLAMPK)
-                dma16(rsrc, dst, voff[i] + (uint32_t)kc_k_offset(k0 + kpos[i], kend, 2), 0u);
+                dma16(rsrc, dst, voff[i] + (uint32_t)kc_k_offset(k0 + kpos[i], kend, ES), 0u);
             else
-                dma16(rsrc, dst, voff[i], (uint32_t)k0 * 2u);
+                dma16(rsrc, dst, voff[i], (uint32_t)k0 * (uint32_t)ES);
         } else {
             if constexpr (CLAMPK)
                 dma16(rsrc, dst, voff[i] + (uint32_t)imin(k0 + kpos[i], kend - 1) * (uint32_t)ld * 2u,
@@ -1239,11 +1245,12 @@ struct DmaOperand {
     __device__ __forceinline__ static void zero_tail(char *lds, int kvalid, int tid, int nthreads) {
         if constexpr (KC) {
             for (int q = tid; q < ROWS * CH; q += nthreads) {
-                const int r = q / CH, c = q % CH;  // logical chunk c: k = 8c..8c+7
-                const int keep = kvalid - 8 * c;
-                if (keep >= 8) continue;
+                const int r = q / CH, c = q % CH;  // logical chunk c: k = EPC*c..
+                const int keep = kvalid - EPC * c;
+                if (keep >= EPC) continue;
                 u32x4 *dst = reinterpret_cast<u32x4 *>(lds + (r * CH + (c ^ swz_kc(r))) * 16);
-                *dst = keep <= 0 ? u32x4{0u, 0u, 0u, 0u} : keep_first(*dst, keep);
+                const u32x4 kept = ES == 2 ? keep_first(*dst, keep) : keep_first_bytes(*dst, keep);
+                *dst = keep <= 0 ? u32x4{0u, 0u, 0u, 0u} : kept;
             }
         } else {
             for (int q = tid; q < (BK - kvalid) * CHR; q += nthreads)
@@ -1260,10 +1267,14 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK;
     constexpr int MF = CF::MF, TM = CF::TM, TN = CF::TN;
     constexpr int NWAVES = CF::WAVES_M * CF::WAVES_N;
+    constexpr int ES = CF::ES, FC = CF::FC;
     constexpr int KS = BK / CF::KSTEP;            // MFMA steps per K-tile
-    constexpr int KCH = CF::KSTEP * 2 / 16;       // 16-byte chunks per step (KC reads)
-    static_assert(CF::ES == 2 && CF::FC == 1, "16-bit operands");
-    static_assert(BK == 64, "LDS rows of 128 bytes (KC layout)");
+    constexpr int KCH = CF::KSTEP * ES / 16;      // 16-byte chunks per step (KC reads)
+    static_assert((ES == 2 && FC == 1) || (ES == 1 && A_KC && B_KC),
+                  "16-bit operands, or K-contiguous 8-bit ones");
+    static_assert(FC == 1 || FC == 2, "fragment chunks");
+    static_assert(BK * ES == 128, "LDS rows of 128 bytes (KC layout)");
+    static_assert(KS % 2 == 0, "fragment slots alternate across K-tiles");
     // B_REG (row-major B with row-major A, one wave per SIMD): B is loaded
     // into registers and transposed on its way to LDS by LoaderRC, so LDS
     // holds it K-contiguous like A; with one wave per SIMD a transposed LDS
@@ -1272,9 +1283,9 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     // reads.
     constexpr bool B_REG = A_KC && !B_KC && NWAVES == 4;
     constexpr bool B_KCL = B_KC || B_REG;  // B's LDS tile is K-contiguous
-    using DA = DmaOperand<BM, BK, NWAVES, MF, A_KC, RAGGED>;
-    using DB = DmaOperand<BN, BK, NWAVES, MF, B_KCL, RAGGED>;
-    using LB = LoaderRC<BN, BK, CF::THREADS>;
+    using DA = DmaOperand<BM, BK, NWAVES, MF, A_KC, RAGGED, ES>;
+    using DB = DmaOperand<BN, BK, NWAVES, MF, B_KCL, RAGGED, ES>;
+    using LB = LoaderRC<BN, B_REG ? BK : 64, CF::THREADS>;  // (unused unless B_REG)
     constexpr int SA = DA::BYTES, SB = DB::BYTES;  // bytes per stage
     char *const ldsA = lds, *const ldsB = lds + 2 * SA;
 
@@ -1314,14 +1325,15 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         lb.template store_one<w>(reinterpret_cast<u32x4 *>(ldsB + stage * SB), tid);
     };
 
-    // per-lane LDS byte offsets of each fragment at step 0, stage 0
+    // per-lane LDS byte offsets of each fragment at step 0, stage 0 (KC: lane
+    // l holds chunks (l / MF) * FC + c, c < FC, of each step, as in k_loop)
     uint32_t a_off[TM], b_off[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int rb0 = wm * CF::WTM + i * MF;
         if constexpr (A_KC) {
             const int r = rb0 + (lane & (MF - 1));
-            a_off[i] = (uint32_t)(r * DA::CH + ((lane / MF) ^ swz_kc(r))) * 16u;
+            a_off[i] = (uint32_t)(r * DA::CH + (((lane / MF) * FC) ^ swz_kc(r))) * 16u;
         } else {
             a_off[i] = (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BM * 2);
         }
@@ -1331,13 +1343,16 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         const int rb0 = wn * CF::WTN + j * MF;
         if constexpr (B_KCL) {
             const int r = rb0 + (lane & (MF - 1));
-            b_off[j] = (uint32_t)(r * DB::CH + ((lane / MF) ^ swz_kc(r))) * 16u;
+            b_off[j] = (uint32_t)(r * DB::CH + (((lane / MF) * FC) ^ swz_kc(r))) * 16u;
         } else {
             b_off[j] = (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BN * 2);
         }
     }
 
-    u32x4 fa[2][TM], fb[2][TN];
+    // Two-chunk fragments (fp8): A single-buffered, as in k_loop (A row i of
+    // the next step is read right after the last MFMA of row i in this step)
+    constexpr bool A1 = FC == 2;
+    u32x4 fa[A1 ? 1 : 2][TM][FC], fb[2][TN][FC];
     // fragment f (A fragments first, then B) of step ks from stage st into slot sl
     auto read_one = [&](int st, auto ks_tag, auto sl_tag, auto f_tag) {
         constexpr int ks = decltype(ks_tag)::value, sl = decltype(sl_tag)::value;
@@ -1354,29 +1369,36 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
             base = ldsB + st * SB;
             off = b_off[f - TM];
         }
-        u32x4 v;
+        u32x4 v[FC];
         if constexpr (kc) {
-            // K-contiguous: chunk ks*KCH + lane/MF of the row; the step's
-            // chunk bits and the lane's never overlap, so XOR adds them
-            v = *reinterpret_cast<const u32x4 *>(base + (off ^ (uint32_t)(ks * KCH * 16)));
+            // K-contiguous: chunks ks*KCH + (lane/MF)*FC + c of the row; the
+            // step's chunk bits, the lane's and c's never overlap, so XOR adds
+            // them
+            Unroll<0, FC>::run([&](auto c_tag) {
+                constexpr int c = decltype(c_tag)::value;
+                constexpr uint32_t cx = (uint32_t)(ks * KCH * 16) ^ (uint32_t)(16 * c);
+                v[c] = *reinterpret_cast<const u32x4 *>(base + (off ^ cx));
+            });
         } else {
             // R-contiguous: the step and half move whole k-rows (k % 4 and
             // bit 3 of k, which the swizzle uses, are the lane's own)
             constexpr uint32_t kstep_rows = MF == 32 ? 16 : 32;
             const u32x2 lo = ds_read_tr16(base + off + ks * kstep_rows * RB);
             const u32x2 hi = ds_read_tr16(base + off + (ks * kstep_rows + 4) * RB);
-            v = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            v[0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        if constexpr (isA) fa[sl][f] = v;
-        else fb[sl][f - TM] = v;
+        Unroll<0, FC>::run([&](auto c_tag) {
+            constexpr int c = decltype(c_tag)::value;
+            if constexpr (isA) fa[A1 ? 0 : sl][f][c] = v[c];
+            else fb[sl][f - TM][c] = v[c];
+        });
     };
     auto mfma_one = [&](auto sl_tag, auto m_tag) {
         constexpr int sl = decltype(sl_tag)::value, m = decltype(m_tag)::value;
         constexpr int i = m / TN, j = m % TN;
-        const u32x4(&xa)[1] = *reinterpret_cast<const u32x4(*)[1]>(&fa[sl][i]);
-        const u32x4(&xb)[1] = *reinterpret_cast<const u32x4(*)[1]>(&fb[sl][j]);
-        if constexpr (MF == 32) acc[i][j] = mfma32<IT, 1>(xb, xa, acc[i][j]);
-        else acc[i][j] = mfma16<IT, 1>(xb, xa, acc[i][j]);
+        constexpr int sa = A1 ? 0 : sl;
+        if constexpr (MF == 32) acc[i][j] = mfma32<IT, FC>(fb[sl][j], fa[sa][i], acc[i][j]);
+        else acc[i][j] = mfma16<IT, FC>(fb[sl][j], fa[sa][i], acc[i][j]);
     };
 
     // prologue: tiles 0 and 1 in flight, wait for tile 0, its step-0
@@ -1464,13 +1486,20 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
                         read_one(cur ^ 1, std::integral_constant<int, 0>{},
                                  std::integral_constant<int, sl ^ 1>{}, fq);
                 };
-                constexpr int r_lo = NR <= NM ? (m < NR ? m : NR) : m * NR / NM;
-                constexpr int r_hi = NR <= NM ? (m < NR ? m + 1 : NR) : (m + 1) * NR / NM;
-                Unroll<r_lo, r_hi>::run([&](auto q_tag) {
-                    constexpr int q = decltype(q_tag)::value;
-                    constexpr int fid = (q == 0) ? 0 : (q <= TN ? TM + q - 1 : q - TN);
-                    read_next(std::integral_constant<int, fid>{});
-                });
+                if constexpr (A1) {
+                    // B column m after MFMA m (m < TN); A row i after its last MFMA
+                    if constexpr (m < TN) read_next(std::integral_constant<int, TM + m>{});
+                    if constexpr (m % TN == TN - 1)
+                        read_next(std::integral_constant<int, m / TN>{});
+                } else {
+                    constexpr int r_lo = NR <= NM ? (m < NR ? m : NR) : m * NR / NM;
+                    constexpr int r_hi = NR <= NM ? (m < NR ? m + 1 : NR) : (m + 1) * NR / NM;
+                    Unroll<r_lo, r_hi>::run([&](auto q_tag) {
+                        constexpr int q = decltype(q_tag)::value;
+                        constexpr int fid = (q == 0) ? 0 : (q <= TN ? TM + q - 1 : q - TN);
+                        read_next(std::integral_constant<int, fid>{});
+                    });
+                }
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
@@ -1805,8 +1834,8 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     tile_epilogue<CF, IT, VEC, (int)sizeof(smem)>(p, acc, m0, n0, smem, tid);
 }
 
-// Large tiles on the LDS-DMA K loop (16-bit operands with 16-byte aligned
-// rows; other operands take gemm_mfma_kernel's element-wise path).
+// Large tiles on the LDS-DMA K loop (16-byte aligned rows: 16-bit operands
+// in every layout, 8-bit ones K-contiguous; the host sends no others).
 template <class CF, int IT, bool A_KC, bool B_KC, bool RAGGED>
 __global__ void __launch_bounds__(CF::THREADS) gemm_dma_kernel(Params p) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK;
@@ -1814,7 +1843,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_dma_kernel(Params p) {
     using Acc = typename AccT<MF>::type;
 
     // two stages of A and B, then the 1 KiB sink of the K loop's idle DMA
-    __shared__ u32x4 smem[2 * (BM + BN) * BK * 2 / 16 + 64];
+    __shared__ u32x4 smem[2 * (BM + BN) * BK * CF::ES / 16 + 64];
     const int tid = threadIdx.x;
     int tile_m, tile_n;
     map_tile(p, blockIdx.x, tile_m, tile_n);
@@ -1830,7 +1859,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_dma_kernel(Params p) {
     });
     dma_k_loop<CF, IT, A_KC, B_KC, RAGGED>(p, m0, n0, kbeg, kend, acc,
                                            reinterpret_cast<char *>(smem), tid);
-    tile_epilogue<CF, IT, true, 2 * (BM + BN) * BK * 2, true>(p, acc, m0, n0, smem, tid);
+    tile_epilogue<CF, IT, true, 2 * (BM + BN) * BK * CF::ES, true>(p, acc, m0, n0, smem, tid);
     wait_vmcnt<0>();  // the sink's loads land before the workgroup's LDS is released
 }
 

@@ -50,6 +50,7 @@ def test_int8_entries_are_in_the_table():
         assert name.startswith("i8_"), name
         if bm is not None:
             assert "_%dx%dx" % (bm, bm) in name, name
+    assert lg.gemm_config_name(I8_DMA).startswith("i8_large_dma8_256x256x")
 
 
 @pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
@@ -85,6 +86,50 @@ def test_m_or_n_contiguous_operands_on_the_vector_path(cid, la, lb, ragged):
     prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="full", c_values="big",
                                lda=lda, ldb=ldb, ldd=N + 3, seed=8050 + cid + 3 * la + lb)
     _check(prob, cid, "i8 cfg%d A%d B%d K%d vector" % (cid, la, lb, K))
+
+
+# the eight-wave LDS-DMA int8 entry: K-contiguous operands (A row-major, B
+# column-major) on 16-byte aligned lines only
+I8_DMA = 17
+
+
+@pytest.mark.parametrize("ragged", [True, False])
+@pytest.mark.parametrize("satf", [0, 1])
+def test_dma_entry_k_contiguous_operands(ragged, satf):
+    """Ragged M and N, a ragged last K-tile (its k >= K part zeroed in LDS) or
+    whole K-tiles, padding lines poisoned, C across the int32 range (wraps or
+    clamps); ldc = ldd a multiple of 4 with satf (register epilogue on the
+    interior tiles), odd otherwise (staged epilogue everywhere)."""
+    M, N = 2 * 256 + 17, 3 * 256 - 5
+    K = 403 if ragged else 512
+    ld = (N + 3) // 4 * 4 + 4 if satf else N + 3
+    prob = W.make_int8_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="full",
+                               c_values="big", satf=satf, lda=_ld16(K), ldb=_ld16(K), ldc=ld,
+                               ldd=ld, seed=8800 + 2 * satf + ragged)
+    _check(prob, I8_DMA, "i8 dma K%d satf %d" % (K, satf))
+
+
+def test_dma_entry_in_place_and_4096():
+    prob = W.make_int8_problem(300, 700, 1000, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+                               values="full", c_values="big", inplace=True, satf=1,
+                               lda=_ld16(1000), ldb=_ld16(1000), ldd=704, seed=8810)
+    _check(prob, I8_DMA, "i8 dma in place")
+
+
+def test_dma_entry_rejects_other_operands():
+    """M- or N-contiguous operands, and lines that are not whole 16-byte
+    units, are not this entry's: forced onto it, the call is rejected."""
+    M, N, K = 100, 90, 160
+    for la, lb in ((ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)):
+        prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="small", seed=8820)
+        with pytest.raises(lg.GemmError) as e:
+            DeviceProblem(prob).run(config=I8_DMA)
+        assert e.value.status == -8
+    prob = W.make_int8_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="small",
+                               lda=K + 1, seed=8821)
+    with pytest.raises(lg.GemmError) as e:
+        DeviceProblem(prob).run(config=I8_DMA)
+    assert e.value.status == -8
 
 
 @pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
