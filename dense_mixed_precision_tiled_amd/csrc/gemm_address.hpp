@@ -63,6 +63,17 @@ LIBGEMM_HD inline int64_t rc8_dword_offset(int r, int k, int R, int kend, int64_
     return (int64_t)kk * ld + rr;
 }
 
+// R-contiguous storage of 8-bit elements: byte offset of the 16-byte chunk
+// holding X(r..r+15, k), with the 16-aligned column r clamped to the chunk
+// holding column R-1 and, when clampk, k clamped to kend-1 (the LDS-DMA
+// loads; ld is a multiple of 16 there).
+LIBGEMM_HD inline int64_t rc8_chunk_offset(int r, int k, int R, int kend, int64_t ld,
+                                           bool clampk) {
+    const int rr = imin(r, (R - 1) & ~15);
+    const int kk = clampk ? imin(k, kend - 1) : k;
+    return (int64_t)kk * ld + rr;
+}
+
 // The in-register transpose of an R-contiguous 8-bit block (4 rows x 16
 // k-rows, one dword per k-row): dword d of row e's K-contiguous chunk holds
 // byte e of the k-rows 4d..4d+3 (a..d), k-row 4d in byte 0.
@@ -96,6 +107,14 @@ LIBGEMM_HD inline int swz_rc(int k, int mf) {
     return mf == 32 ? (k & 3) << 2 : ((k & 3) | ((k >> 1) & 4)) << 1;
 }
 
+// R-contiguous 8-bit tile: k-row k holds R bytes as R/16 chunks; chunk c of
+// k-row k sits at slot c ^ swz_rc8(k).  A 16-lane group of the transposed
+// reads (ds_read_b64_tr_b8) touches 8 consecutive k-rows at one chunk, and a
+// half-wave two adjacent chunks (an even and an odd one); the XOR moves
+// whole 32-byte pairs by k % 8, so the half-wave's 16 chunks, 64 banks, are
+// distinct.  Needs R >= 256 (16 chunks).
+LIBGEMM_HD inline int swz_rc8(int k) { return (k & 7) << 1; }
+
 // Direct global -> LDS loads write 16 bytes per lane to consecutive LDS
 // chunks (lane l of an instruction to chunk q0 + l).  The source a lane
 // reads is therefore the chunk that belongs at that slot:
@@ -110,6 +129,11 @@ LIBGEMM_HD inline void dma_kc_source(int q, int ch, int &row, int &chunk) {
 LIBGEMM_HD inline void dma_rc_source(int q, int chr, int mf, int &krow, int &chunk) {
     krow = q / chr;
     chunk = (q % chr) ^ swz_rc(krow, mf);
+}
+// (8-bit R-contiguous tile: rows 16 * ((q % chr) ^ swz_rc8(k-row)) .. + 15)
+LIBGEMM_HD inline void dma_rc8_source(int q, int chr, int &krow, int &chunk) {
+    krow = q / chr;
+    chunk = (q % chr) ^ swz_rc8(krow);
 }
 
 // Transposed operand read (ds_read_b64_tr_b16) from an R-contiguous tile with
@@ -131,6 +155,24 @@ LIBGEMM_HD inline int tr_read_offset(int lane, int mf, int ks, int h, int rb, in
     const int krow = ks * kstep + kgrp + 4 * h + f;
     const int row = rb + rsub + 4 * q;
     return krow * rowbytes + (((row / 8) ^ swz_rc(krow, mf)) * 16) + (row % 8) * 2;
+}
+
+// Transposed 8-bit operand read (ds_read_b64_tr_b8) from an R-contiguous
+// tile with rowbytes bytes per k-row: in each group of 16 lanes, lane L
+// supplies the address of 8 consecutive bytes and lane j of the group
+// receives byte j % 8 of lane 2f + (j % 16) / 8 as its element f (f = 0..7;
+// probed on the GPU).  For the 32x32 MFMA operand of rows rb..rb+31 (fc
+// 16-byte chunks of k per lane, kstep k values per step) at step ks, chunk c
+// and half h (k offset 8h inside the chunk), lane L addresses k-row
+// ks*kstep + 16*fc*(L / 32) + 16c + 8h + (L % 16) / 2 at row
+// rb + 16 * ((L / 16) % 2) + 8 * (L % 2).  Then lane j holds X(rb + j % 32, k)
+// for the 8 k-values k = ks*kstep + 16*fc*(j / 32) + 16c + 8h + 0..7, bytes
+// 8h..8h+7 of its operand chunk c, as the MFMA expects.
+LIBGEMM_HD inline int tr8_read_offset(int lane, int fc, int ks, int kstep, int c, int h, int rb,
+                                      int rowbytes) {
+    const int krow = ks * kstep + 16 * fc * (lane / 32) + 16 * c + 8 * h + (lane % 16) / 2;
+    const int row = rb + 16 * ((lane / 16) % 2) + 8 * (lane % 2);
+    return krow * rowbytes + ((row / 16) ^ swz_rc8(krow)) * 16 + row % 16;
 }
 
 // Output tile of workgroup w.  The device hands workgroups to its xcds XCDs

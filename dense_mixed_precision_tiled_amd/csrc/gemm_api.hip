@@ -119,11 +119,6 @@ bool needs_vec(int id) {
     return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16 || id == CFG_LARGE_DMA8_16 ||
            id == CFG_I8_LARGE_DMA8 || id == CFG_F8_LARGE_DMA8;
 }
-// The 8-bit LDS-DMA entries also need both operands K-contiguous (as the
-// kernels see them: row-major A, column-major B).
-bool needs_kc(int id) {
-    return id == CFG_I8_LARGE_DMA8 || id == CFG_F8_LARGE_DMA8;
-}
 // the register-staged large tile of each input class
 int class_large(int klass) {
     return klass == 1 ? CFG_I8_LARGE8 : klass == 2 ? CFG_F8_LARGE : CFG_LARGE8;
@@ -188,20 +183,17 @@ int select_config(int64_t M, int64_t N, int64_t K, int klass, int cus) {
 // 16x16x32 MFMA (measured 6-8% faster at 4096^3: that MFMA sustains a higher
 // clock under the power limit); an N- or M-contiguous operand would need
 // transposed LDS reads, which cost more than the register-staged transpose
-// of the eight-wave tile.  fp8: with K-contiguous aligned operands and whole
-// K-tiles, the eight-wave LDS-DMA tile (4096^3 ~6% faster than the four-wave
-// register-staged one; its ragged-K kernel spills a few registers in the K
-// loop, so a ragged K keeps the four-wave tile).  The four-wave fp8 tile
-// (512 registers) spills inside its K loop when an operand is M- or
-// N-contiguous (the transposing loads), so those take the 128x128 fp8 tile:
-// 4096^3 with row-major B 289 -> 152 us.  int8 keeps its eight-wave
-// register-staged tile: the LDS-DMA int8 entry measured on par with it.
-int refine_large(int id, bool aligned, int layoutA, int layoutB, int64_t K) {
+// of the eight-wave tile.  fp8 with 16-byte aligned lines: the eight-wave
+// LDS-DMA tile in every layout (4096^3: K-contiguous ~6% faster than the
+// four-wave register-staged tile, on par at K = 4100; M- or N-contiguous
+// operands 83-108 us against 140-176 us on the 128x128 tile, which they took
+// because the four-wave tile spills with its transposing loads).  int8
+// keeps its eight-wave register-staged tile: the LDS-DMA int8 entry measured
+// on par with it for K-contiguous operands and slower otherwise.
+int refine_large(int id, bool aligned, int layoutA, int layoutB) {
     const bool kc = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
     if (id == CFG_LARGE8 && aligned && kc) return CFG_LARGE_DMA16;
-    if (id == CFG_F8_LARGE && aligned && kc && K % CfgLargeDma8F8::BK == 0)
-        return CFG_F8_LARGE_DMA8;
-    if (id == CFG_F8_LARGE && aligned && !kc) return CFG_F8_MEDIUM;
+    if (id == CFG_F8_LARGE && aligned) return CFG_F8_LARGE_DMA8;
     return id;
 }
 
@@ -446,14 +438,13 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     }
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng_used : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng_used : 0u;
-    const bool kc_ops = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
-    if ((needs_vec(id) && !p.vec_ok) || (needs_kc(id) && !kc_ops)) {
+    if (needs_vec(id) && !p.vec_ok) {
         // a forced entry that cannot run these operands is an error; the
         // dispatcher's choice falls back to the register-staged large tile
         if (config_id >= 0) return GEMM_ERR_INVALID_CONFIG;
         id = class_large(klass);
     }
-    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB, K);
+    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB);
     const Entry &E = kTable[id];
     const int osz = out_size(out_dtype);
     // register epilogue (vector C, D and bias access): aligned row-major C and D
@@ -741,7 +732,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
                             1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr, 0);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
     return refine_large(select_config(M, N, K, input_class(in_dtype), topology().cus), true,
-                        layoutA, layoutB, K);
+                        layoutA, layoutB);
 }
 
 }  // extern "C"

@@ -57,11 +57,11 @@ using CfgMediumF8 = TileCfg<128, 128, 128, 2, 2, 32, 1, 2>;
 using CfgSmallF8 = TileCfg<64, 64, 128, 2, 2, 32, 1, 2>;
 using CfgSkinnyF8 = TileCfg<16, 128, 256, 1, 4, 16, 1, 2>;
 
-// The LDS-DMA K loop for 8-bit operands that are both K-contiguous (row-major
-// A, column-major B, 16-byte aligned rows): eight waves of 128x64 (two per
-// SIMD, 128 accumulators each), LDS rows of 128 bytes (BK = 128 values).  No
-// operand passes through registers on its way to LDS, which leaves room for
-// the fp8 MFMA's two-chunk fragments at two waves per SIMD.
+// The LDS-DMA K loop for 8-bit operands (16-byte aligned rows, every layout):
+// eight waves of 128x64 (two per SIMD, 128 accumulators each), 128 k values
+// per K-tile; M- or N-contiguous operands are read with the transposing byte
+// reads.  No operand passes through registers on its way to LDS, which
+// leaves room for the fp8 MFMA's two-chunk fragments at two waves per SIMD.
 using CfgLargeDma8I8 = TileCfg<256, 256, 128, 2, 4, 32, 1>;
 using CfgLargeDma8F8 = TileCfg<256, 256, 128, 2, 4, 32, 1, 2>;
 
@@ -155,17 +155,11 @@ hipError_t launch_dma_one(const Params &p, dim3 grid, hipStream_t s) {
 
 template <class CF, int IT>
 hipError_t launch_dma_layouts(const Params &p, int akc, int bkc, dim3 grid, hipStream_t s) {
-    if constexpr (CF::ES == 1) {
-        // 8-bit operands: K-contiguous A and B only (the host sends no others)
-        if (!akc || !bkc) return hipErrorInvalidValue;
-        return launch_dma_one<CF, IT, true, true>(p, grid, s);
-    } else {
-        if (akc)
-            return bkc ? launch_dma_one<CF, IT, true, true>(p, grid, s)
-                       : launch_dma_one<CF, IT, true, false>(p, grid, s);
-        return bkc ? launch_dma_one<CF, IT, false, true>(p, grid, s)
-                   : launch_dma_one<CF, IT, false, false>(p, grid, s);
-    }
+    if (akc)
+        return bkc ? launch_dma_one<CF, IT, true, true>(p, grid, s)
+                   : launch_dma_one<CF, IT, true, false>(p, grid, s);
+    return bkc ? launch_dma_one<CF, IT, false, true>(p, grid, s)
+               : launch_dma_one<CF, IT, false, false>(p, grid, s);
 }
 
 template <class CF, int IT>

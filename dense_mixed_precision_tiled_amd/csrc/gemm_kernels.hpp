@@ -50,6 +50,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 // dtype codes of the C ABI (C, D and out_dtype)
@@ -1143,9 +1144,9 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
 //   K-contiguous (row-major A, column-major B): [rows][BK] in 16-byte chunks,
 //     read with ds_read_b128 (one chunk per lane and MFMA operand, two for
 //     the fp8 MFMAs); 16-bit and 8-bit values alike (rows of 128 bytes);
-//   R-contiguous (row-major B, column-major A; 16-bit only): [BK][rows],
-//     read with the transposing ds_read_b64_tr_b16 (two per lane and MFMA
-//     operand).
+//   R-contiguous (row-major B, column-major A): [BK][rows], read with the
+//     transposing ds_read_b64_tr_b16 (two per lane and MFMA operand) or, for
+//     8-bit values, ds_read_b64_tr_b8 (two per 16-byte chunk; 32x32 MFMA).
 // The XOR swizzles (gemm_address.hpp) are applied on the global side: lane l
 // of a DMA instruction fills LDS chunk q0 + l, so it fetches the chunk that
 // belongs in that slot.
@@ -1180,25 +1181,29 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const char *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+__device__ __forceinline__ u32x2 ds_read_tr8(const char *p) {
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LIBGEMM_LDS i32x2 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, char *lds_dst, uint32_t voff,
                                       uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LIBGEMM_LDS void *)lds_dst, 16, (int)voff,
                                              (int)soff, 0, 0);
 }
 
-// One operand's DMA for the K loop: ROWS x BK tile of ES-byte values (16-bit,
-// or 8-bit when K-contiguous), KC or R-contiguous storage, NWAVES waves
-// sharing the tile's 1 KiB DMA blocks.
+// One operand's DMA for the K loop: ROWS x BK tile of ES-byte values (16-bit
+// or 8-bit), KC or R-contiguous storage, NWAVES waves sharing the tile's
+// 1 KiB DMA blocks.
 template <int ROWS, int BK, int NWAVES, int MF, bool KC, bool CLAMPK, int ES = 2>
 struct DmaOperand {
     static constexpr int BYTES = ROWS * BK * ES;
     static constexpr int NI = BYTES / 1024 / NWAVES;  // DMA instructions per wave
     static_assert(BYTES % (1024 * NWAVES) == 0, "1 KiB DMA blocks per wave");
-    static_assert(ES == 2 || KC, "8-bit operands: K-contiguous only");
-    static constexpr int EPC = 16 / ES;      // elements per 16-byte chunk
-    static constexpr int CH = BK * ES / 16;  // KC: chunks per row
-    static constexpr int CHR = ROWS / 8;     // RC: chunks per k-row
-    static_assert(KC || ROWS >= 128, "the R-contiguous swizzle needs 16 chunks per k-row");
+    static constexpr int EPC = 16 / ES;        // elements per 16-byte chunk
+    static constexpr int CH = BK * ES / 16;    // KC: chunks per row
+    static constexpr int CHR = ROWS * ES / 16; // RC: chunks per k-row
+    static_assert(KC || CHR >= 16, "the R-contiguous swizzles need 16 chunks per k-row");
     uint32_t voff[NI];  // byte offset at k0 = 0 (CLAMPK: without the k part)
     int kpos[NI];       // CLAMPK: k position of the chunk (KC) or the k-row (RC)
 
@@ -1212,10 +1217,14 @@ struct DmaOperand {
                 kpos[i] = EPC * c;
                 voff[i] =
                     (uint32_t)kc_chunk_offset(r0 + a, CLAMPK ? 0 : EPC * c, R, 1, ld, ES, false);
-            } else {
+            } else if constexpr (ES == 2) {
                 dma_rc_source(q, CHR, MF, a, c);  // a = k-row, rows 8c..8c+7
                 kpos[i] = a;
                 voff[i] = (uint32_t)rc_chunk_offset(r0 + 8 * c, CLAMPK ? 0 : a, R, 1, ld, false);
+            } else {
+                dma_rc8_source(q, CHR, a, c);  // a = k-row, rows 16c..16c+15
+                kpos[i] = a;
+                voff[i] = (uint32_t)rc8_chunk_offset(r0 + 16 * c, CLAMPK ? 0 : a, R, 1, ld, false);
             }
         }
     }
@@ -1232,11 +1241,12 @@ struct DmaOperand {
             else
                 dma16(rsrc, dst, voff[i], (uint32_t)k0 * (uint32_t)ES);
         } else {
+            constexpr uint32_t es = ES;
             if constexpr (CLAMPK)
-                dma16(rsrc, dst, voff[i] + (uint32_t)imin(k0 + kpos[i], kend - 1) * (uint32_t)ld * 2u,
+                dma16(rsrc, dst, voff[i] + (uint32_t)imin(k0 + kpos[i], kend - 1) * (uint32_t)ld * es,
                       0u);
             else
-                dma16(rsrc, dst, voff[i], (uint32_t)k0 * (uint32_t)ld * 2u);
+                dma16(rsrc, dst, voff[i], (uint32_t)k0 * (uint32_t)ld * es);
         }
     }
 
@@ -1254,7 +1264,7 @@ struct DmaOperand {
             }
         } else {
             for (int q = tid; q < (BK - kvalid) * CHR; q += nthreads)
-                reinterpret_cast<u32x4 *>(lds + (kvalid + q / CHR) * ROWS * 2)[q % CHR] =
+                reinterpret_cast<u32x4 *>(lds + (kvalid + q / CHR) * ROWS * ES)[q % CHR] =
                     u32x4{0u, 0u, 0u, 0u};
         }
     }
@@ -1270,8 +1280,8 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     constexpr int ES = CF::ES, FC = CF::FC;
     constexpr int KS = BK / CF::KSTEP;            // MFMA steps per K-tile
     constexpr int KCH = CF::KSTEP * ES / 16;      // 16-byte chunks per step (KC reads)
-    static_assert((ES == 2 && FC == 1) || (ES == 1 && A_KC && B_KC),
-                  "16-bit operands, or K-contiguous 8-bit ones");
+    static_assert((ES == 2 && FC == 1) || (ES == 1 && (MF == 32 || (A_KC && B_KC))),
+                  "16-bit operands, or 8-bit ones (R-contiguous: the 32x32 MFMA)");
     static_assert(FC == 1 || FC == 2, "fragment chunks");
     static_assert(BK * ES == 128, "LDS rows of 128 bytes (KC layout)");
     static_assert(KS % 2 == 0, "fragment slots alternate across K-tiles");
@@ -1335,7 +1345,8 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
             const int r = rb0 + (lane & (MF - 1));
             a_off[i] = (uint32_t)(r * DA::CH + (((lane / MF) * FC) ^ swz_kc(r))) * 16u;
         } else {
-            a_off[i] = (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BM * 2);
+            a_off[i] = ES == 2 ? (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BM * 2)
+                               : (uint32_t)tr8_read_offset(lane, FC, 0, CF::KSTEP, 0, 0, rb0, BM);
         }
     }
 #pragma unroll
@@ -1345,7 +1356,8 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
             const int r = rb0 + (lane & (MF - 1));
             b_off[j] = (uint32_t)(r * DB::CH + (((lane / MF) * FC) ^ swz_kc(r))) * 16u;
         } else {
-            b_off[j] = (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BN * 2);
+            b_off[j] = ES == 2 ? (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BN * 2)
+                               : (uint32_t)tr8_read_offset(lane, FC, 0, CF::KSTEP, 0, 0, rb0, BN);
         }
     }
 
@@ -1359,7 +1371,7 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         constexpr int f = decltype(f_tag)::value;
         constexpr bool isA = f < TM;
         constexpr bool kc = isA ? A_KC : B_KCL;
-        constexpr int RB = isA ? BM * 2 : BN * 2;  // R-contiguous: bytes per k-row
+        constexpr int RB = (isA ? BM : BN) * ES;  // R-contiguous: bytes per k-row
         const char *base;
         uint32_t off;
         if constexpr (isA) {
@@ -1379,13 +1391,23 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
                 constexpr uint32_t cx = (uint32_t)(ks * KCH * 16) ^ (uint32_t)(16 * c);
                 v[c] = *reinterpret_cast<const u32x4 *>(base + (off ^ cx));
             });
-        } else {
+        } else if constexpr (ES == 2) {
             // R-contiguous: the step and half move whole k-rows (k % 4 and
             // bit 3 of k, which the swizzle uses, are the lane's own)
             constexpr uint32_t kstep_rows = MF == 32 ? 16 : 32;
             const u32x2 lo = ds_read_tr16(base + off + ks * kstep_rows * RB);
             const u32x2 hi = ds_read_tr16(base + off + (ks * kstep_rows + 4) * RB);
             v[0] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            // R-contiguous 8-bit: chunk c's halves are k-rows 16c and 16c + 8
+            // on from the step's; the swizzle uses k % 8, the lane's own
+            Unroll<0, FC>::run([&](auto c_tag) {
+                constexpr int c = decltype(c_tag)::value;
+                constexpr uint32_t k0 = (uint32_t)(ks * CF::KSTEP + 16 * c);
+                const u32x2 lo = ds_read_tr8(base + off + k0 * RB);
+                const u32x2 hi = ds_read_tr8(base + off + (k0 + 8) * RB);
+                v[c] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            });
         }
         Unroll<0, FC>::run([&](auto c_tag) {
             constexpr int c = decltype(c_tag)::value;
@@ -1834,8 +1856,8 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     tile_epilogue<CF, IT, VEC, (int)sizeof(smem)>(p, acc, m0, n0, smem, tid);
 }
 
-// Large tiles on the LDS-DMA K loop (16-byte aligned rows: 16-bit operands
-// in every layout, 8-bit ones K-contiguous; the host sends no others).
+// Large tiles on the LDS-DMA K loop (operands with 16-byte aligned rows, in
+// every layout; the host sends no others).
 template <class CF, int IT, bool A_KC, bool B_KC, bool RAGGED>
 __global__ void __launch_bounds__(CF::THREADS) gemm_dma_kernel(Params p) {
     constexpr int BM = CF::BM, BN = CF::BN, BK = CF::BK;

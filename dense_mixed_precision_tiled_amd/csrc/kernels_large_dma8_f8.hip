@@ -1,6 +1,6 @@
 // Kernel instantiations for the "fp8_large_dma8" tile-table entry (eight-wave
-// LDS-DMA K loop, 32x32x64 MFMA, OCP fp8 E4M3 inputs; K-contiguous A and
-// B only), in a translation unit of its own so the library builds in
+// LDS-DMA K loop, 32x32x64 MFMA, OCP fp8 E4M3 inputs; every operand
+// layout), in a translation unit of its own so the library builds in
 // parallel.
 #include "gemm_configs.hpp"
 

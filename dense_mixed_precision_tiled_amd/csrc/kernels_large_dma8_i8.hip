@@ -1,7 +1,7 @@
 // Kernel instantiations for the "i8_large_dma8" tile-table entry (eight-wave
 // LDS-DMA K loop, 32x32x32 MFMA, int8 inputs, int32 accumulator and output;
-// K-contiguous A and B only), in a translation unit of its own so the
-// library builds in parallel.
+// every operand layout), in a translation unit of its own so the library
+// builds in parallel.
 #include "gemm_configs.hpp"
 
 namespace libgemm {

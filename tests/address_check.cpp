@@ -258,6 +258,83 @@ static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves) {
     free(filled);
 }
 
+// The 8-bit DMA tile (ROWS x BK bytes, fc 16-byte chunks per lane and MFMA
+// operand, the 32x32 MFMA): every byte is tracked by the element it holds.
+// The DMA placement fills each LDS chunk once; the fragment reads (KC: fc
+// 16-byte reads; RC: 2*fc transposed reads with the exchange probed on the
+// GPU) must give lane j the bytes X(rb + j % 32, k) for
+// k = ks*kstep + 16*fc*(j / 32) + 16c + e, e = 0..15, chunk c < fc; and each
+// half-wave of a transposed read must touch 64 distinct 4-byte banks.
+static void check_dma_tile8(int ROWS, int BK, int fc, bool KC, int nwaves) {
+    const int bytes = ROWS * BK, chunks = bytes / 16;
+    const int ni = bytes / 1024 / nwaves;
+    const int kstep = 32 * fc;
+    if (bytes % (1024 * nwaves)) { fail("dma8 blocks", ROWS, BK, nwaves, 0); return; }
+    std::vector<int> lds((size_t)bytes, -1), filled((size_t)chunks, 0);
+    auto id = [](int r, int k) { return r * 4096 + k; };
+    for (int w = 0; w < nwaves; ++w)
+        for (int i = 0; i < ni; ++i)
+            for (int l = 0; l < 64; ++l) {
+                const int q = (w * ni + i) * 64 + l;
+                int a, c;
+                if (KC) dma_kc_source(q, BK / 16, a, c); else dma_rc8_source(q, ROWS / 16, a, c);
+                for (int e = 0; e < 16; ++e)   // KC: row a, k = 16c+e; RC: k-row a, row 16c+e
+                    lds[(size_t)q * 16 + e] = KC ? id(a, 16 * c + e) : id(16 * c + e, a);
+                filled[(size_t)q]++;
+            }
+    for (int q = 0; q < chunks; ++q)
+        if (filled[(size_t)q] != 1) fail("dma8 chunk filled times", q, filled[(size_t)q], ROWS, KC);
+    for (int ks = 0; ks < BK / kstep; ++ks)
+        for (int rb = 0; rb < ROWS; rb += 32) {
+            int got[64][32];
+            if (KC) {
+                const int kch = kstep / 16;
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int r = rb + lane % 32;
+                    const uint32_t off =
+                        (uint32_t)(r * (BK / 16) + (((lane / 32) * fc) ^ swz_kc(r))) * 16u;
+                    for (int c = 0; c < fc; ++c) {
+                        const uint32_t a = off ^ (uint32_t)(ks * kch * 16) ^ (uint32_t)(16 * c);
+                        for (int e = 0; e < 16; ++e) got[lane][16 * c + e] = lds[a + e];
+                    }
+                }
+            } else {
+                for (int c = 0; c < fc; ++c)
+                    for (int h = 0; h < 2; ++h) {
+                        int in[64][8];
+                        int off[64];
+                        for (int L = 0; L < 64; ++L) {
+                            off[L] = tr8_read_offset(L, fc, ks, kstep, c, h, rb, ROWS);
+                            if (off[L] % 8 || off[L] < 0 || off[L] + 8 > bytes)
+                                fail("tr8 offset", off[L], L, ks, h);
+                            for (int e = 0; e < 8; ++e) in[L][e] = lds[(size_t)off[L] + e];
+                        }
+                        for (int half = 0; half < 2; ++half) {
+                            int used[64] = {0};
+                            for (int L = 32 * half; L < 32 * half + 32; ++L)
+                                for (int d = 0; d < 2; ++d) used[(off[L] / 4 + d) % 64]++;
+                            for (int b = 0; b < 64; ++b)
+                                if (used[b] != 1) fail("tr8 bank use", b, used[b], ks, rb);
+                        }
+                        // the instruction's exchange: lane j element f <- lane
+                        // 16*(j/16) + 2f + (j%16)/8, byte j%8
+                        for (int j = 0; j < 64; ++j)
+                            for (int f = 0; f < 8; ++f)
+                                got[j][16 * c + 8 * h + f] =
+                                    in[16 * (j / 16) + 2 * f + (j % 16) / 8][j % 8];
+                    }
+            }
+            for (int lane = 0; lane < 64; ++lane)
+                for (int c = 0; c < fc; ++c)
+                    for (int e = 0; e < 16; ++e) {
+                        const int r = rb + lane % 32;
+                        const int k = ks * kstep + 16 * fc * (lane / 32) + 16 * c + e;
+                        ++g_checked;
+                        if (got[lane][16 * c + e] != id(r, k)) fail("fragment8 value", lane, e, r, k);
+                    }
+        }
+}
+
 // raster_tile must hit every tile of the grid exactly once.
 static void check_raster(int tiles_m, int tiles_n, int group_m, int xcds, int skew) {
     const int T = tiles_m * tiles_n;
@@ -310,6 +387,10 @@ int main() {
     for (int nw : {4, 8})
         for (int mf : {32, 16})
             for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, nw);
+    // the 8-bit DMA tiles: 256 rows x 128 bytes, eight waves, int8 (one
+    // chunk per lane) and fp8 (two), both storage orders
+    for (int fc : {1, 2})
+        for (bool kc : {true, false}) check_dma_tile8(256, 128, fc, kc, 8);
     // the raster: grids of one tile to several rounds per CU, ragged groups,
     // every group height and XCD count the host uses, with and without skew
     const int grids[][2] = {{1, 1}, {1, 7}, {7, 1}, {16, 16}, {64, 64}, {63, 65}, {5, 33}, {32, 32}, {3, 200}};

@@ -72,17 +72,12 @@ def test_dispatcher_shape_classes(lib):
     assert pick8(4096, 4096, 4096).startswith("i8_large8")
     assert pick8(16, 16384, 16384).startswith("i8_skinny")
     assert pick8(256, 256, 256).startswith("i8_small")
-    # fp8: with K-contiguous operands the eight-wave LDS-DMA tile for whole
-    # K-tiles, the four-wave register-staged tile for a ragged K; the 128x128
-    # tile when an operand is M- or N-contiguous (the large tile spills there)
+    # fp8: the eight-wave LDS-DMA tile in every layout (aligned operands)
     E4 = lg.GEMM_FP8_E4M3
-    assert names[lg.gemm_select_config(4096, 4096, 4096, R, Cm, E4, F32, F32)] == \
-        "fp8_large_dma8_256x256x128_w2x4_mfma32x32x64"
-    assert names[lg.gemm_select_config(4096, 4096, 4100, R, Cm, E4, F32, F32)] == \
-        "fp8_large_256x256x128_w2x2_mfma32x32x64"
-    for la, lb in ((R, R), (Cm, Cm), (Cm, R)):
-        assert names[lg.gemm_select_config(4096, 4096, 4096, la, lb, E4, F32, F32)] == \
-            "fp8_medium_128x128x128_w2x2_mfma32x32x64"
+    for la, lb in ((R, Cm), (R, R), (Cm, Cm), (Cm, R)):
+        for K in (4096, 4100):
+            assert names[lg.gemm_select_config(4096, 4096, K, la, lb, E4, F32, F32)] == \
+                "fp8_large_dma8_256x256x128_w2x4_mfma32x32x64"
     assert lg.gemm_select_config(-1, 4, 4, R, R, F16, F32, F32) == -1
     assert lg.gemm_select_config(4, 4, 4, 7, R, F16, F32, F32) == -5
     assert lg.gemm_select_config(4, 4, 4, R, R, F32, F32, F32) == -4

@@ -67,8 +67,8 @@ def test_m_or_n_contiguous_operands_on_the_vector_path(cid, fmt, la, lb):
                 cid, fmt, la, lb, K, values))
 
 
-# the eight-wave LDS-DMA fp8 entry: K-contiguous operands (A row-major, B
-# column-major) on 16-byte aligned lines only
+# the eight-wave LDS-DMA fp8 entry: 16-byte aligned lines only (M- or
+# N-contiguous operands take the transposing byte reads)
 F8_DMA = 18
 
 
@@ -77,22 +77,23 @@ def test_fp8_dma_entry_is_in_the_table():
 
 
 @pytest.mark.parametrize("fmt", [FP8_E4M3, FP8_E5M2])
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, COL_MAJOR), (ROW_MAJOR, ROW_MAJOR),
+                                   (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)])
 @pytest.mark.parametrize("ragged", [True, False])
-def test_fp8_dma_entry_k_contiguous_operands(fmt, ragged):
+def test_fp8_dma_entry_every_layout(fmt, la, lb, ragged):
     """Ragged M and N, a ragged last K-tile (its k >= K part zeroed in LDS)
-    or whole K-tiles, padding lines poisoned; exact and rounded data, with
-    C on the staged (odd ldd) and on the register epilogue (ldc = ldd a
-    multiple of 4)."""
+    or whole K-tiles, padding lines poisoned; exact data with C on the
+    staged epilogue (odd ldd), rounded data with C on the register epilogue
+    (ldc = ldd a multiple of 4)."""
     M, N = 2 * 256 + 17, 3 * 256 - 5
     K = 403 if ragged else 512
-    ld16 = (K + 15) // 16 * 16 + 16
-    for values, exact in (("int", True), ("uniform", False)):
-        for ld in (N + 3, (N + 3) // 4 * 4 + 4):
-            prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=fmt,
-                                  values=values, c_values="int" if exact else "normal",
-                                  lda=ld16, ldb=ld16, ldc=ld, ldd=ld,
-                                  seed=9700 + 10 * fmt + 2 * ragged + (ld % 4 == 0))
-            _check(prob, exact, F8_DMA, "fp8 dma fmt%d K%d ldd%d %s" % (fmt, K, ld, values))
+    lda = ((K if la == ROW_MAJOR else M) + 15) // 16 * 16 + 16
+    ldb = ((N if lb == ROW_MAJOR else K) + 15) // 16 * 16 + 16
+    for values, exact, ld in (("int", True, N + 3), ("uniform", False, (N + 3) // 4 * 4 + 4)):
+        prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, in_dtype=fmt, values=values,
+                              c_values="int" if exact else "normal", lda=lda, ldb=ldb, ldc=ld,
+                              ldd=ld, seed=9700 + 10 * fmt + 2 * ragged + 4 * la + 8 * lb)
+        _check(prob, exact, F8_DMA, "fp8 dma fmt%d A%d B%d K%d %s" % (fmt, la, lb, K, values))
 
 
 def test_fp8_dma_entry_output_modes():
@@ -101,24 +102,19 @@ def test_fp8_dma_entry_output_modes():
              dict(out_dtype=BF16, c_values="normal", ldd=N + 8),
              dict(out_dtype=F32, c_values="normal", inplace=True, ldd=N + 5)]
     for mode in modes:
-        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=FP8_E4M3,
-                              values="normal", lda=K, ldb=K, seed=9750, **mode)
+        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR, in_dtype=FP8_E4M3,
+                              values="normal", lda=K, ldb=(N + 15) // 16 * 16, seed=9750, **mode)
         _check(prob, False, F8_DMA, "fp8 dma out=%d" % prob.out_dtype)
 
 
-def test_fp8_dma_entry_rejects_other_operands():
+def test_fp8_dma_entry_rejects_unaligned_lines():
     M, N, K = 100, 90, 160
-    for la, lb in ((ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)):
+    for la, lb, lda, ldb in ((ROW_MAJOR, COL_MAJOR, K + 1, K), (ROW_MAJOR, ROW_MAJOR, K, N + 3)):
         prob = W.make_problem(M, N, K, layoutA=la, layoutB=lb, in_dtype=FP8_E4M3, values="int",
-                              seed=9760)
+                              lda=lda, ldb=ldb, seed=9761)
         with pytest.raises(lg.GemmError) as e:
             DeviceProblem(prob).run(config=F8_DMA)
         assert e.value.status == -8
-    prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, in_dtype=FP8_E4M3,
-                          values="int", lda=K + 1, seed=9761)
-    with pytest.raises(lg.GemmError) as e:
-        DeviceProblem(prob).run(config=F8_DMA)
-    assert e.value.status == -8
 
 
 @pytest.mark.parametrize("cid", sorted(F8_ENTRY_TILE))

@@ -88,48 +88,48 @@ def test_m_or_n_contiguous_operands_on_the_vector_path(cid, la, lb, ragged):
     _check(prob, cid, "i8 cfg%d A%d B%d K%d vector" % (cid, la, lb, K))
 
 
-# the eight-wave LDS-DMA int8 entry: K-contiguous operands (A row-major, B
-# column-major) on 16-byte aligned lines only
+# the eight-wave LDS-DMA int8 entry: 16-byte aligned lines only (M- or
+# N-contiguous operands take the transposing byte reads)
 I8_DMA = 17
 
 
+@pytest.mark.parametrize("la,lb", [(ROW_MAJOR, COL_MAJOR), (ROW_MAJOR, ROW_MAJOR),
+                                   (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)])
 @pytest.mark.parametrize("ragged", [True, False])
-@pytest.mark.parametrize("satf", [0, 1])
-def test_dma_entry_k_contiguous_operands(ragged, satf):
+def test_dma_entry_every_layout(la, lb, ragged):
     """Ragged M and N, a ragged last K-tile (its k >= K part zeroed in LDS) or
-    whole K-tiles, padding lines poisoned, C across the int32 range (wraps or
-    clamps); ldc = ldd a multiple of 4 with satf (register epilogue on the
-    interior tiles), odd otherwise (staged epilogue everywhere)."""
+    whole K-tiles, padding lines poisoned, C across the int32 range: wrapping
+    with an odd ldd (staged epilogue), clamping (satf) with ldc = ldd a
+    multiple of 4 (register epilogue on the interior tiles)."""
     M, N = 2 * 256 + 17, 3 * 256 - 5
     K = 403 if ragged else 512
-    ld = (N + 3) // 4 * 4 + 4 if satf else N + 3
-    prob = W.make_int8_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="full",
-                               c_values="big", satf=satf, lda=_ld16(K), ldb=_ld16(K), ldc=ld,
-                               ldd=ld, seed=8800 + 2 * satf + ragged)
-    _check(prob, I8_DMA, "i8 dma K%d satf %d" % (K, satf))
+    lda = _ld16(K if la == ROW_MAJOR else M)
+    ldb = _ld16(N if lb == ROW_MAJOR else K)
+    for satf in (0, 1):
+        ld = (N + 3) // 4 * 4 + 4 if satf else N + 3
+        prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="full",
+                                   c_values="big", satf=satf, lda=lda, ldb=ldb, ldc=ld, ldd=ld,
+                                   seed=8800 + 2 * satf + ragged + 4 * la + 8 * lb)
+        _check(prob, I8_DMA, "i8 dma A%d B%d K%d satf %d" % (la, lb, K, satf))
 
 
-def test_dma_entry_in_place_and_4096():
-    prob = W.make_int8_problem(300, 700, 1000, layoutA=ROW_MAJOR, layoutB=COL_MAJOR,
+def test_dma_entry_in_place():
+    prob = W.make_int8_problem(300, 700, 1000, layoutA=ROW_MAJOR, layoutB=ROW_MAJOR,
                                values="full", c_values="big", inplace=True, satf=1,
-                               lda=_ld16(1000), ldb=_ld16(1000), ldd=704, seed=8810)
+                               lda=_ld16(1000), ldb=_ld16(700), ldd=704, seed=8810)
     _check(prob, I8_DMA, "i8 dma in place")
 
 
-def test_dma_entry_rejects_other_operands():
-    """M- or N-contiguous operands, and lines that are not whole 16-byte
-    units, are not this entry's: forced onto it, the call is rejected."""
+def test_dma_entry_rejects_unaligned_lines():
+    """Lines that are not whole 16-byte units are not this entry's: forced
+    onto it, the call is rejected."""
     M, N, K = 100, 90, 160
-    for la, lb in ((ROW_MAJOR, ROW_MAJOR), (COL_MAJOR, COL_MAJOR), (COL_MAJOR, ROW_MAJOR)):
-        prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="small", seed=8820)
+    for la, lb, lda, ldb in ((ROW_MAJOR, COL_MAJOR, K + 1, K), (ROW_MAJOR, ROW_MAJOR, K, N + 3)):
+        prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="small", lda=lda,
+                                   ldb=ldb, seed=8821)
         with pytest.raises(lg.GemmError) as e:
             DeviceProblem(prob).run(config=I8_DMA)
         assert e.value.status == -8
-    prob = W.make_int8_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="small",
-                               lda=K + 1, seed=8821)
-    with pytest.raises(lg.GemmError) as e:
-        DeviceProblem(prob).run(config=I8_DMA)
-    assert e.value.status == -8
 
 
 @pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
