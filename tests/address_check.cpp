@@ -335,6 +335,56 @@ static void check_dma_tile8(int ROWS, int BK, int fc, bool KC, int nwaves) {
         }
 }
 
+// The DMA kernels' global side: every lane's 16-byte load of every DMA
+// instruction, tile, K slice and K-tile, composed as DmaOperand does
+// (init + issue, the clamped form when clampk), must lie inside the
+// operand's 16-byte range and hold one of its elements, and an in-range
+// chunk must be the one its LDS slot expects.
+static void check_dma_global(int ROWS, int BK, int ES, int MF, bool KC, int nwaves, int R, int K,
+                             int64_t ld, int kps, bool clampk) {
+    const int bytes = ROWS * BK * ES, ni = bytes / 1024 / nwaves, epc = 16 / ES;
+    const int ch = BK * ES / 16, chr = ROWS * ES / 16;
+    const int64_t range = KC ? operand_range(R, K, ld, ES) : operand_range(K, R, ld, ES);
+    const int splits = (K + kps - 1) / kps;
+    for (int r0 = 0; r0 < R; r0 += ROWS)
+        for (int z = 0; z < splits; ++z) {
+            const int kbeg = z * kps, kend = K < kbeg + kps ? K : kbeg + kps;
+            for (int k0 = kbeg; k0 < kend; k0 += BK)
+                for (int q = 0; q < nwaves * ni * 64; ++q) {
+                    int a, c;
+                    int64_t off;
+                    int row, k;  // the element the chunk starts with, unclamped
+                    if (KC) {
+                        dma_kc_source(q, ch, a, c);
+                        const int64_t voff = kc_chunk_offset(r0 + a, clampk ? 0 : epc * c, R, 1, ld,
+                                                             ES, false);
+                        off = clampk ? voff + kc_k_offset(k0 + epc * c, kend, ES) : voff + (int64_t)k0 * ES;
+                        row = r0 + a;
+                        k = k0 + epc * c;
+                    } else {
+                        if (ES == 2) dma_rc_source(q, chr, MF, a, c); else dma_rc8_source(q, chr, a, c);
+                        const int r = r0 + epc * c;
+                        const int64_t voff = ES == 2 ? rc_chunk_offset(r, clampk ? 0 : a, R, 1, ld, false)
+                                                     : rc8_chunk_offset(r, clampk ? 0 : a, R, 1, ld, false);
+                        off = clampk ? voff + (int64_t)imin(k0 + a, kend - 1) * ld * ES
+                                     : voff + (int64_t)k0 * ld * ES;
+                        row = r;
+                        k = k0 + a;
+                    }
+                    ++g_checked;
+                    if (off < 0 || off % 16 != 0 || off + 16 > range)
+                        fail("dma load out of range", off, range, row, k);
+                    const int64_t line = off / (ld * ES), first = (off % (ld * ES)) / ES;
+                    if (line >= (KC ? R : K) || first >= (KC ? K : R))
+                        fail("dma chunk holds no element", off, line, first, ES);
+                    if (row < R && k < kend) {
+                        const int64_t want = KC ? ((int64_t)row * ld + k) * ES : ((int64_t)k * ld + row) * ES;
+                        if (off != want) fail("dma wrong chunk", off, want, row, k);
+                    }
+                }
+        }
+}
+
 // raster_tile must hit every tile of the grid exactly once.
 static void check_raster(int tiles_m, int tiles_n, int group_m, int xcds, int skew) {
     const int T = tiles_m * tiles_n;
@@ -387,6 +437,24 @@ int main() {
     for (int nw : {4, 8})
         for (int mf : {32, 16})
             for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, nw);
+    // the DMA loads' global offsets over the problem sides above (16-byte
+    // lines as the DMA entries require), 16-bit and 8-bit, both orders, the
+    // plain and the clamped form
+    for (const Side &s : kc_sides)
+        for (int es : {2, 1})
+            for (bool kc : {true, false}) {
+                const int bk = 128 / es;
+                const int kps = ((s.kps + bk - 1) / bk) * bk;
+                const bool ragged = (s.K % bk) != 0 || (kps % bk) != 0;
+                const int inner = kc ? s.K : s.R;
+                const int64_t ld = ((int64_t)inner * es + 15) / 16 * 16 / es + (kc ? 0 : 16 / es);
+                for (int nw : {4, 8})
+                    for (bool clampk : {true, false}) {
+                        if (!clampk && ragged) continue;  // the kernels clamp whenever K is ragged
+                        if (es == 1 && nw == 4) continue;
+                        check_dma_global(256, bk, es, 32, kc, nw, s.R, s.K, ld, kps, clampk);
+                    }
+            }
     // the 8-bit DMA tiles: 256 rows x 128 bytes, eight waves, int8 (one
     // chunk per lane) and fp8 (two), both storage orders
     for (int fc : {1, 2})

@@ -3,7 +3,12 @@ loaders compose their byte offsets from the functions of
 ``csrc/gemm_address.hpp``; ``address_check.cpp`` composes them the same way
 for every tile, thread, chunk and K-tile of a set of problems (the HGEMM
 workload's ragged K among them) and checks that every 16-byte chunk read lies
-inside the operand and holds one of its elements.  It also walks the
+inside the operand and holds one of its elements.  The LDS-DMA loads are
+checked the same way on the global side (16-bit and 8-bit, both storage
+orders, plain and clamped K), and simulated on the LDS side: placement,
+swizzles, the transposed reads with the lane exchange probed on the GPU,
+every lane's MFMA operand and, for the 8-bit transposed reads, the banks
+each half-wave touches.  It also walks the
 workgroup-to-tile raster (``raster_tile``) over grids, group heights, XCD
 counts and the skewed column order, and checks that every tile is computed
 exactly once.  Built with g++ under
