@@ -1,8 +1,9 @@
 """gemm_run_noalloc (no device allocation: split-K partial sums in the
 library's fixed scratch) against gemm_run through the C ABI: two calls in a
 row, the second with a smaller problem, each bit-identical to gemm_run (the
-same kernels and split) and within the oracle's bounds.  Runs alone in a
-fresh process and after the other GPU tests."""
+same kernels and split) and within the oracle's bounds; and captured into a
+HIP graph and replayed.  Runs alone in a fresh process and after the other
+GPU tests."""
 import numpy as np
 import pytest
 import torch
@@ -52,3 +53,46 @@ def test_noalloc_matches_gemm_run_on_two_calls_second_smaller(values, exact):
         assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), prob.name
         compare(prob, region(prob, got), region(prob, oracle_whole(prob)), exact,
                 label="noalloc " + prob.name)
+
+
+def _args(dp):
+    p = dp.prob
+    return (p.M, p.N, p.K, dp.A.data_ptr(), p.lda, p.layoutA, dp.B.data_ptr(), p.ldb, p.layoutB,
+            None if dp.C is None else dp.C.data_ptr(), p.ldc, dp.D.data_ptr(), p.ldd,
+            p.in_dtype, p.acc_dtype, p.out_dtype, p.satf)
+
+
+def _eager(dp, fn):
+    dp.reset_D()
+    st = fn(*_args(dp), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lg.gemm_status_string(st)
+    return dp.result().copy()
+
+
+@pytest.mark.parametrize("shape", [(16, 4096, 8192), (520, 530, 384)])
+def test_noalloc_replayed_from_a_graph(shape):
+    """The callers gemm_run_noalloc is for include code under graph capture:
+    captured once (the split-K shape captures the partial-sum kernel and the
+    reduction over the library's scratch), replayed three times with eager
+    calls of both entry points on other data between the replays (the same
+    scratch), every replay equals the eager result bit for bit."""
+    M, N, K = shape
+    dp = DeviceProblem(W.make_problem(M, N, K, values="int", c_values="int", seed=7200 + M))
+    dq = DeviceProblem(W.make_problem(M, N, K, values="int", c_values="int", seed=7300 + M))
+    want = _eager(dp, lg.gemm_run_noalloc)
+    other = _eager(dq, lg.gemm_run_noalloc)
+    log("case: graph capture of gemm_run_noalloc %dx%dx%d" % shape)
+    dp.reset_D()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = lg.gemm_run_noalloc(*_args(dp), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lg.gemm_status_string(st)
+    for rep in range(3):
+        eager = _eager(dq, lg.gemm_run_noalloc if rep % 2 == 0 else lg.gemm_run)
+        assert np.array_equal(eager.view(np.uint8), other.view(np.uint8)), rep
+        dp.reset_D()
+        torch.cuda.synchronize()
+        g.replay()
+        got = dp.result().copy()
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), "replay %d" % rep
