@@ -1552,7 +1552,9 @@ __device__ __forceinline__ f32x4 acc_group(const T &t, int g) {
 // Finish one BM x BN tile from its accumulators: each lane owns 4
 // consecutive columns of one row per register group.  smem (SMEM_BYTES of
 // LDS) is free for staging: the K loop's reads of it are complete.
-template <class CF, int IT, bool VEC, int SMEM_BYTES, bool AGPR = false>
+// EPIX_OK: interior tiles may take the extended epilogue (fp32 out) in
+// registers; otherwise it always goes through the staged loop.
+template <class CF, int IT, bool VEC, int SMEM_BYTES, bool AGPR = false, bool EPIX_OK = false>
 __device__ __forceinline__ void tile_epilogue(const Params &p,
                                               typename AccT<CF::MF>::type (&acc)[CF::TM][CF::TN],
                                               int m0, int n0, u32x4 *smem, int tid) {
@@ -1582,8 +1584,10 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
     // check and an element-wise fallback per group, made this unrolled code
     // three times larger: that cost int8 20% (epilogue spills) and the
     // 16384^2 x 1024 shape, 16 tiles per CU, 25%.)
-    auto direct = [&](auto out_tag) {
+    auto direct = [&](auto out_tag, auto epix_tag) {
         constexpr int OUT = decltype(out_tag)::value;
+        // EPIX: the extended epilogue (scale, bias, activation) in registers
+        constexpr bool EPIX = decltype(epix_tag)::value;
         // Float outputs load C ahead of the stores, for RB row blocks at a
         // time: a wait for a load also waits for every earlier store, so
         // loads issued between stores serialise them.  RB row blocks of C
@@ -1596,6 +1600,20 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
             return n0 + wn * CF::WTN + j * MF + acc_col<MF>(lane, g);
         };
         auto row_of = [&](int i) { return m0 + wm * CF::WTM + i * MF + acc_row<MF>(lane); };
+        // EPIX: the bias of the lane's columns, loaded before any store (the
+        // same for every row block; a load between stores would wait for them)
+        f32x4 bcol[EPIX ? TN : 1][EPIX ? NG : 1];
+        if constexpr (EPIX) {
+            Unroll<0, TN>::run([&](auto jj) {
+                Unroll<0, NG>::run([&](auto gg) {
+                    constexpr int j = decltype(jj)::value, g = decltype(gg)::value;
+                    const int col = col_of(j, g);
+                    bcol[j][g] = (p.bias && !p.bias_rows && col + 4 <= p.N)
+                                     ? *reinterpret_cast<const f32x4 *>(p.bias + col)
+                                     : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                });
+            });
+        }
         Unroll<0, TM / RB>::run([&](auto bb) {
             constexpr int i0 = decltype(bb)::value * RB;
             // raw C bits (fp32: 4 words per group, 16-bit: 2), converted at the store
@@ -1615,6 +1633,15 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
                     });
                 });
             }
+            // bias by row (a column-major D's transposed problem): one value per row
+            float brow[RB];
+            if constexpr (EPIX) {
+                Unroll<0, RB>::run([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
+                    const int row = row_of(i0 + r);
+                    brow[r] = (p.bias && p.bias_rows) ? p.bias[row < p.M ? row : 0] : 0.0f;
+                });
+            }
             Unroll<0, RB>::run([&](auto rr) {
                 constexpr int r = decltype(rr)::value, i = i0 + r;
                 const int row = row_of(i);
@@ -1630,8 +1657,19 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
                         if constexpr (IT == IT_I8) {
                             finish4<OUT, true, false>(p, row, col, v);
                         } else if (col + 4 <= p.N) {
-                            finish4<OUT, true, false, true>(p, row, col,
-                                                            v + c_from_raw<OUT>(cpre[r][j][g]));
+                            if constexpr (EPIX) {
+                                // alpha * sum + beta * C + bias, then the activation
+                                f32x4 x = p.alpha * v;
+                                if (p.C) x += p.beta * c_from_raw<OUT>(cpre[r][j][g]);
+                                if (p.bias) {
+                                    x += p.bias_rows ? f32x4{brow[r], brow[r], brow[r], brow[r]}
+                                                     : bcol[j][g];
+                                }
+                                finish4<OUT, true, true, true>(p, row, col, x);
+                            } else {
+                                finish4<OUT, true, false, true>(p, row, col,
+                                                                v + c_from_raw<OUT>(cpre[r][j][g]));
+                            }
                         }
                     });
                 });
@@ -1658,7 +1696,7 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
                             if (col_of(j, g) == pc) v = acc_group<AGPR>(acc[i][j], g);
                         });
                     });
-                    if (pc >= 0) finish4<OUT, false, false>(p, row_of(i), pc, v);
+                    if (pc >= 0) finish4<OUT, false, EPIX>(p, row_of(i), pc, v);
                 });
             }
         }
@@ -1666,12 +1704,19 @@ __device__ __forceinline__ void tile_epilogue(const Params &p,
     // (kernels with element-wise operand loads serve unaligned operands, a
     // slow path anyway: they finish through the staged loop only)
     if constexpr (VEC) {
+        using NoX = std::false_type;
         if (ncols && !p.epi) {
-            if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{});
-            else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{});
-            else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{});
-            else direct(std::integral_constant<int, DT_BF16>{});
+            if constexpr (IT == IT_I8) direct(std::integral_constant<int, DT_I32>{}, NoX{});
+            else if (p.out_dtype == DT_F32) direct(std::integral_constant<int, DT_F32>{}, NoX{});
+            else if (p.out_dtype == DT_F16) direct(std::integral_constant<int, DT_F16>{}, NoX{});
+            else direct(std::integral_constant<int, DT_BF16>{}, NoX{});
             return;
+        }
+        if constexpr (IT != IT_I8 && EPIX_OK) {
+            if (ncols && p.epi && p.out_dtype == DT_F32) {
+                direct(std::integral_constant<int, DT_F32>{}, std::true_type{});
+                return;
+            }
         }
     }
     // staged path: one MF-row block per wave at a time in the wave's own LDS
@@ -1853,7 +1898,7 @@ __global__ void __launch_bounds__(CF::THREADS) gemm_mfma_kernel(Params p) {
     });
 
     k_loop<CF, IT, A_KC, B_KC, VEC, RAGGED>(p, m0, n0, kbeg, kend, acc, sA, sB, tid);
-    tile_epilogue<CF, IT, VEC, (int)sizeof(smem)>(p, acc, m0, n0, smem, tid);
+    tile_epilogue<CF, IT, VEC, (int)sizeof(smem), false, !RAGGED>(p, acc, m0, n0, smem, tid);
 }
 
 // Large tiles on the LDS-DMA K loop (operands with 16-byte aligned rows, in
