@@ -300,7 +300,7 @@ typedef struct {
  * a bias pointer that is not 16-byte aligned, take the element-wise store
  * path of edge tiles.  With an fp32 D (leading dimensions of C and D
  * multiples of 4, 16-byte aligned C, D and bias) and K a multiple of the
- * tile's K step, the register-staged large tiles apply the whole epilogue
+ * tile's K step, the register-staged entries apply the whole epilogue
  * from registers on interior tiles; other calls stage each tile through LDS
  * first.  GELU costs about 20 vector instructions per output element.
  */
