@@ -301,8 +301,8 @@ typedef struct {
  * path of edge tiles.  With an fp32 D (leading dimensions of C and D
  * multiples of 4, 16-byte aligned C, D and bias) and K a multiple of the
  * tile's K step, the register-staged entries apply the whole epilogue
- * from registers on interior tiles; other calls stage each tile through LDS
- * first.  GELU costs about 20 vector instructions per output element.
+ * from registers; other calls stage each tile through LDS first.  GELU
+ * costs about 20 vector instructions per output element.
  */
 int gemm_run_ex(int64_t M, int64_t N, int64_t K,
                 const void *A, int64_t lda, int layoutA,
