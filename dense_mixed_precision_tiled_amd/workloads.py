@@ -186,6 +186,15 @@ def scale_rows(prob: Problem, frac: float, factor: float, seed: int) -> np.ndarr
     return rows
 
 
+def pattern_int(r, k):
+    """X(r, k) = (131r + 71k + rk mod 97) mod 5 - 2 for broadcastable 64-bit
+    integer arrays r, k (numpy or torch, on any device): integer values in
+    [-2, 2], exact in every input type, with no short period along r or k,
+    that need no storage to reproduce -- for operands too large to draw and
+    keep on the host (any rows of them can be rebuilt for the oracle)."""
+    return (131 * r + 71 * k + (r * k) % 97) % 5 - 2
+
+
 def sample_indices(M: int, N: int, count: int, seed: int):
     """Seeded (row, col) pairs, without repetition when count <= M*N."""
     rng = np.random.default_rng(seed)

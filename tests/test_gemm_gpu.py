@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import dense_mixed_precision_tiled_amd as lg
+import oracle
 from dense_mixed_precision_tiled_amd import workloads as W
 from dense_mixed_precision_tiled_amd.workloads import BF16, COL_MAJOR, F16, F32, ROW_MAJOR
 from gpu_util import (DeviceProblem, check_padding, compare, log, oracle_full, oracle_whole,
@@ -109,6 +110,40 @@ def test_multi_round_ragged_skewed_raster(values, exact):
     prob = W.make_problem(4100, 4610, 1000, values=values, c_values="normal" if values ==
                           "uniform" else "int", seed=20311, name="4100x4610x1000 +C")
     _whole_check(prob, exact)
+
+
+def test_operand_past_the_32_bit_byte_range():
+    """A of 65600 x 32768 fp16 (4.3 GB) lies past the byte range that the
+    buffer loads' 32-bit offsets address: the call takes the element-wise
+    loads (64-bit offsets; the operand copy for alignment would be as large,
+    so none is made) and must stay exact.  Integer-valued data from
+    pattern_int; rows on both sides of the 4 GiB mark, the first and the last
+    rows compared bit for bit with the oracle."""
+    M, K, N = 65600, 32768, 48
+    assert M * K * 2 > (1 << 32)
+    log("case: A past 4 GiB, %dx%dx%d" % (M, N, K))
+    dev = torch.device("cuda")
+    A = torch.empty(M, K, dtype=torch.float16, device=dev)
+    kk = torch.arange(K, device=dev, dtype=torch.int64)[None, :]
+    for r0 in range(0, M, 4096):
+        rr = torch.arange(r0, min(M, r0 + 4096), device=dev, dtype=torch.int64)[:, None]
+        A[r0:r0 + rr.shape[0]] = W.pattern_int(rr, kk).to(torch.float16)
+    kb, nb = np.arange(K)[:, None], np.arange(N)[None, :]
+    Bh = W.pattern_int(kb + 3, nb).astype(np.float16)
+    B = torch.from_numpy(Bh).to(dev)
+    D = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    st = lg.gemm_run(M, N, K, A.data_ptr(), K, ROW_MAJOR, B.data_ptr(), N, ROW_MAJOR, None, N,
+                     D.data_ptr(), N, F16, F32, F32, 0, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, lg.gemm_status_string(st)
+    rows = np.array([0, 1, 32767, 32768, 65535, 65536, 65537, M - 2, M - 1])
+    got = D[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del A, D
+    As = W.pattern_int(rows[:, None], np.arange(K)[None, :]).astype(np.float16)
+    ref = np.zeros((len(rows), N), np.float32)
+    oracle.gemm(len(rows), N, K, As.view(np.uint16).ravel(), K, ROW_MAJOR,
+                Bh.view(np.uint16).ravel(), N, ROW_MAJOR, None, N, ref.ravel(), N,
+                F16, F32, F32, 0)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 # ------------------------------------------------- every tile-table entry
