@@ -20,7 +20,9 @@ The ceilings the GEMM is read against are workloads too (lib/libgemm_measure.so)
 ``--workload mfma_peak_32`` / ``mfma_peak_16`` (a stream of independent
 v_mfma_f32_32x32x16_f16 / 16x16x32_f16 on random fp16 operands in registers,
 one workgroup of four waves per CU) and ``--workload copy`` (a 16-byte
-load/store copy of 512 MiB).
+load/store copy of 512 MiB); ``--workload vendor_4096_f16`` times the
+platform's BLAS (torch.mm with fp32 output) on the headline problem, for
+context only.
 """
 from __future__ import annotations
 
@@ -144,6 +146,9 @@ MEASURE_WORKLOADS = {
                      "held in registers, 8 waves (two per SIMD) per CU, no memory traffic",
                      "TFLOP/s"),
     "copy": ("device copy of 512 MiB with 16-byte loads and stores (read + write bytes)", "GB/s"),
+    "vendor_4096_f16": ("the platform's BLAS on the headline problem, for context: torch.mm "
+                        "(hipBLASLt) of the same fp16 row-major A and B with fp32 output",
+                        "TFLOP/s"),
 }
 MEASURE_LIB = os.path.join(ROOT, "dense_mixed_precision_tiled_amd", "lib", "libgemm_measure.so")
 PEAK_I8_TOPS = 5000.0  # MI355X dense int8 MFMA, published
@@ -417,6 +422,19 @@ def measure(args):
         peak, bound, dtype = PEAK_TFLOPS, "mfma", "f16"
         config = {"workload": desc, "mfma": "32x32x16" if mf == 32 else "16x16x32",
                   "workgroups": blocks, "threads": threads, "rounds": iters}
+    elif args.workload == "vendor_4096_f16":
+        from dense_mixed_precision_tiled_amd import workloads as W
+        prob = W.w_4096_f16("uniform")
+        A = torch.from_numpy(prob.A.view(np.int16)).to(dev).view(torch.float16)
+        B = torch.from_numpy(prob.B.view(np.int16)).to(dev).view(torch.float16)
+        D = torch.empty(prob.M, prob.N, dtype=torch.float32, device=dev)
+        work = float(prob.flops)
+
+        def launch():
+            torch.mm(A, B, out_dtype=torch.float32, out=D)
+            return 0
+        peak, bound, dtype = PEAK_TFLOPS, "mfma", "f16"
+        config = {"workload": desc, "M": prob.M, "N": prob.N, "K": prob.K}
     else:
         nbytes = 512 << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
@@ -450,8 +468,10 @@ def measure(args):
     mean_ms = sum(durations_ms) / len(durations_ms)
     achieved = work / (mean_ms * 1e-3) / scale
     out = {
-        "metric": "%s ceiling, workload %s" % ("MFMA" if bound == "mfma" else "HBM copy",
-                                               args.workload),
+        "metric": ("vendor library TFLOP/s (2MNK/t), workload %s" % args.workload
+                   if args.workload.startswith("vendor") else
+                   "%s ceiling, workload %s" % ("MFMA" if bound == "mfma" else "HBM copy",
+                                                args.workload)),
         "value": round(work * args.steps / wall / scale, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
