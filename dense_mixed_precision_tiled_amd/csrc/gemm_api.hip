@@ -104,21 +104,26 @@ const Entry kTable[] = {
      CfgLargeDma8I8::BK, 0, 1, launch_large_dma8_i8},
     {"fp8_large_dma8_256x256x128_w2x4_mfma32x32x64", CfgLargeDma8F8::BM, CfgLargeDma8F8::BN,
      CfgLargeDma8F8::BK, 0, 2, launch_large_dma8_fp8},
+    {"i8_large_dma_256x256x128_w2x2_mfma16x16x64", CfgLargeDmaI8_16::BM, CfgLargeDmaI8_16::BN,
+     CfgLargeDmaI8_16::BK, 0, 1, launch_large_dma16_i8},
 };
 constexpr int kNumConfigs = sizeof(kTable) / sizeof(kTable[0]);
 enum { CFG_LARGE = 0, CFG_MEDIUM = 1, CFG_SMALL = 2, CFG_SKINNY = 3, CFG_LARGE8 = 4,
        CFG_I8_LARGE8 = 5, CFG_I8_MEDIUM = 6, CFG_I8_SMALL = 7, CFG_I8_SKINNY = 8,
        CFG_F8_LARGE = 9, CFG_F8_MEDIUM = 10, CFG_F8_SMALL = 11, CFG_F8_SKINNY = 12,
        CFG_LARGE_DMA = 13, CFG_TINY = 14, CFG_LARGE_DMA16 = 15, CFG_LARGE_DMA8_16 = 16,
-       CFG_I8_LARGE_DMA8 = 17, CFG_F8_LARGE_DMA8 = 18 };
+       CFG_I8_LARGE_DMA8 = 17, CFG_F8_LARGE_DMA8 = 18, CFG_I8_LARGE_DMA16 = 19 };
 
 // Entries whose kernels load operands straight into LDS: 16-byte aligned
 // operands only (vec_ok); others run the entry of the same tile shape
 // with register-staged loads.
 bool needs_vec(int id) {
     return id == CFG_LARGE_DMA || id == CFG_LARGE_DMA16 || id == CFG_LARGE_DMA8_16 ||
-           id == CFG_I8_LARGE_DMA8 || id == CFG_F8_LARGE_DMA8;
+           id == CFG_I8_LARGE_DMA8 || id == CFG_F8_LARGE_DMA8 || id == CFG_I8_LARGE_DMA16;
 }
+// Entries for K-contiguous operands only (as the kernels see them: row-major
+// A, column-major B).
+bool needs_kc(int id) { return id == CFG_I8_LARGE_DMA16; }
 // the register-staged large tile of each input class
 int class_large(int klass) {
     return klass == 1 ? CFG_I8_LARGE8 : klass == 2 ? CFG_F8_LARGE : CFG_LARGE8;
@@ -183,16 +188,20 @@ int select_config(int64_t M, int64_t N, int64_t K, int klass, int cus) {
 // 16x16x32 MFMA (measured 6-8% faster at 4096^3: that MFMA sustains a higher
 // clock under the power limit); an N- or M-contiguous operand would need
 // transposed LDS reads, which cost more than the register-staged transpose
-// of the eight-wave tile.  fp8 with 16-byte aligned lines: the eight-wave
-// LDS-DMA tile in every layout (4096^3: K-contiguous ~6% faster than the
-// four-wave register-staged tile, on par at K = 4100; M- or N-contiguous
-// operands 83-108 us against 140-176 us on the 128x128 tile, which they took
-// because the four-wave tile spills with its transposing loads).  int8
-// keeps its eight-wave register-staged tile: the LDS-DMA int8 entry measured
-// on par with it for K-contiguous operands and slower otherwise.
-int refine_large(int id, bool aligned, int layoutA, int layoutB) {
+// of the eight-wave tile.  int8: the same four-wave shape with the 16x16x64
+// MFMA for K-contiguous aligned operands and whole K-tiles (4096^3 ~10%
+// faster than the eight-wave register-staged tile; its ragged-K kernel
+// spills, so a ragged K keeps the register-staged tile, as do the other
+// layouts).  fp8 with 16-byte aligned lines: the eight-wave LDS-DMA tile in
+// every layout (4096^3: K-contiguous ~6% faster than the four-wave
+// register-staged tile, on par at K = 4100; M- or N-contiguous operands
+// 83-108 us against 140-176 us on the 128x128 tile, which they took because
+// the four-wave tile spills with its transposing loads).
+int refine_large(int id, bool aligned, int layoutA, int layoutB, int64_t K) {
     const bool kc = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
     if (id == CFG_LARGE8 && aligned && kc) return CFG_LARGE_DMA16;
+    if (id == CFG_I8_LARGE8 && aligned && kc && K % CfgLargeDmaI8_16::BK == 0)
+        return CFG_I8_LARGE_DMA16;
     if (id == CFG_F8_LARGE && aligned) return CFG_F8_LARGE_DMA8;
     return id;
 }
@@ -438,13 +447,14 @@ int run(int config_id, int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     }
     p.a_bytes = p.vec_ok ? (uint32_t)a_rng_used : 0u;
     p.b_bytes = p.vec_ok ? (uint32_t)b_rng_used : 0u;
-    if (needs_vec(id) && !p.vec_ok) {
+    const bool kc_ops = layoutA == GEMM_ROW_MAJOR && layoutB == GEMM_COL_MAJOR;
+    if ((needs_vec(id) && !p.vec_ok) || (needs_kc(id) && !kc_ops)) {
         // a forced entry that cannot run these operands is an error; the
         // dispatcher's choice falls back to the register-staged large tile
         if (config_id >= 0) return GEMM_ERR_INVALID_CONFIG;
         id = class_large(klass);
     }
-    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB);
+    if (auto_choice) id = refine_large(id, p.vec_ok != 0, layoutA, layoutB, K);
     const Entry &E = kTable[id];
     const int osz = out_size(out_dtype);
     // register epilogue (vector C, D and bias access): aligned row-major C and D
@@ -732,7 +742,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K, int layoutA, int layoutB
                             1 + N, nullptr, 1 + N, in_dtype, acc_dtype, out_dtype, nullptr, 0);
     if (st != GEMM_OK && st != GEMM_ERR_NULL_PTR) return st;
     return refine_large(select_config(M, N, K, input_class(in_dtype), topology().cus), true,
-                        layoutA, layoutB);
+                        layoutA, layoutB, K);
 }
 
 }  // extern "C"

@@ -205,11 +205,14 @@ const char *gemm_status_string(int status);
  *                16-byte aligned operand lines, or a negative gemm_status_t
  *                if the arguments are invalid.  Entries whose kernels load
  *                operands straight into LDS ("large_dma...", and the 8-bit
- *                "i8_large_dma8..." and "fp8_large_dma8...") accept only
- *                16-byte aligned operand lines: with other operands gemm_run
- *                runs the register-staged 256x256 entry of the input type
- *                instead, and gemm_run_config forced to such an entry
- *                returns GEMM_ERR_INVALID_CONFIG.
+ *                "i8_large_dma..." and "fp8_large_dma8...") accept only
+ *                16-byte aligned operand lines, and "i8_large_dma_..." (the
+ *                four-wave 16x16x64 one) only K-contiguous operands (A
+ *                row-major and B column-major as the kernels see them: a
+ *                column-major D swaps and flips them): with other operands
+ *                gemm_run runs the register-staged 256x256 entry of the
+ *                input type instead, and gemm_run_config forced to such an
+ *                entry returns GEMM_ERR_INVALID_CONFIG.
  */
 int gemm_num_configs(void);
 const char *gemm_config_name(int config_id);

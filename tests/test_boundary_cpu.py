@@ -69,7 +69,12 @@ def test_dispatcher_shape_classes(lib):
     assert pick(1024, 1024, 1024).startswith("small")
     I8, I32 = lg.GEMM_I8, lg.GEMM_I32
     pick8 = lambda M, N, K: names[lg.gemm_select_config(M, N, K, R, Cm, I8, I32, I32)]
-    assert pick8(4096, 4096, 4096).startswith("i8_large8")
+    # int8: K-contiguous, aligned, whole K-tiles -> the four-wave LDS-DMA
+    # tile; a ragged K or another layout -> the eight-wave register-staged one
+    assert pick8(4096, 4096, 4096) == "i8_large_dma_256x256x128_w2x2_mfma16x16x64"
+    assert pick8(4096, 4096, 4100).startswith("i8_large8")
+    assert names[lg.gemm_select_config(4096, 4096, 4096, R, R, I8, I32, I32)].startswith(
+        "i8_large8")
     assert pick8(16, 16384, 16384).startswith("i8_skinny")
     assert pick8(256, 256, 256).startswith("i8_small")
     # fp8: the eight-wave LDS-DMA tile in every layout (aligned operands)

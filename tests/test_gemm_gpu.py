@@ -172,11 +172,12 @@ def _entry_shapes():
 
 
 def test_config_ids_match_table():
-    # 16-bit entries here; the int8 entries (ids 5..8, 17) and the fp8
+    # 16-bit entries here; the int8 entries (ids 5..8, 17, 19) and the fp8
     # entries (ids 9..12, 18) are covered by test_int8_gpu and test_fp8_gpu
-    assert lg.gemm_num_configs() == len(ENTRY_TILE) + 10
+    assert lg.gemm_num_configs() == len(ENTRY_TILE) + 11
     assert lg.gemm_config_name(17).startswith("i8_")
     assert lg.gemm_config_name(18).startswith("fp8_")
+    assert lg.gemm_config_name(19).startswith("i8_")
     assert lg.gemm_config_name(13).startswith("large_dma")
     for cid in range(5, 9):
         assert lg.gemm_config_name(cid).startswith("i8_")

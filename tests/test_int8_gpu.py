@@ -51,6 +51,7 @@ def test_int8_entries_are_in_the_table():
         if bm is not None:
             assert "_%dx%dx" % (bm, bm) in name, name
     assert lg.gemm_config_name(I8_DMA).startswith("i8_large_dma8_256x256x")
+    assert lg.gemm_config_name(I8_DMA16).startswith("i8_large_dma_256x256x128_w2x2_mfma16x16x64")
 
 
 @pytest.mark.parametrize("cid", sorted(I8_ENTRY_TILE))
@@ -111,6 +112,42 @@ def test_dma_entry_every_layout(la, lb, ragged):
                                    c_values="big", satf=satf, lda=lda, ldb=ldb, ldc=ld, ldd=ld,
                                    seed=8800 + 2 * satf + ragged + 4 * la + 8 * lb)
         _check(prob, I8_DMA, "i8 dma A%d B%d K%d satf %d" % (la, lb, K, satf))
+
+
+# the four-wave LDS-DMA int8 entry (16x16x64 MFMA): K-contiguous operands on
+# 16-byte aligned lines only
+I8_DMA16 = 19
+
+
+@pytest.mark.parametrize("ragged", [True, False])
+@pytest.mark.parametrize("satf", [0, 1])
+def test_four_wave_dma_entry(ragged, satf):
+    """Ragged M and N, a ragged last K-tile or whole K-tiles, padding lines
+    poisoned, C across the int32 range: wrapping with an odd ldd (staged
+    epilogue), clamping with ldc = ldd a multiple of 4 (register epilogue)."""
+    M, N = 2 * 256 + 17, 3 * 256 - 5
+    K = 403 if ragged else 512
+    for inplace in (False, True):
+        ld = (N + 3) // 4 * 4 + 4 if satf else N + 3
+        prob = W.make_int8_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="full",
+                                   c_values="big", satf=satf, inplace=inplace,
+                                   lda=_ld16(K), ldb=_ld16(K), ldc=ld, ldd=ld,
+                                   seed=8830 + 2 * satf + ragged + 4 * inplace)
+        _check(prob, I8_DMA16, "i8 dma4 K%d satf %d inplace %d" % (K, satf, inplace))
+
+
+def test_four_wave_dma_entry_rejects_other_operands():
+    """M- or N-contiguous operands and unaligned lines: forced onto the
+    entry, the call is rejected."""
+    M, N, K = 100, 90, 160
+    cases = [(ROW_MAJOR, ROW_MAJOR, K, _ld16(N)), (COL_MAJOR, COL_MAJOR, _ld16(M), K),
+             (COL_MAJOR, ROW_MAJOR, _ld16(M), _ld16(N)), (ROW_MAJOR, COL_MAJOR, K + 1, K)]
+    for la, lb, lda, ldb in cases:
+        prob = W.make_int8_problem(M, N, K, layoutA=la, layoutB=lb, values="small", lda=lda,
+                                   ldb=ldb, seed=8840)
+        with pytest.raises(lg.GemmError) as e:
+            DeviceProblem(prob).run(config=I8_DMA16)
+        assert e.value.status == -8, (la, lb)
 
 
 def test_dma_entry_in_place():
