@@ -96,6 +96,17 @@ LIBGEMM_HD inline int64_t operand_range(int64_t outer, int64_t inner, int64_t ld
 // eight rows 8 apart, land in eight different 16-byte bank groups.
 LIBGEMM_HD inline int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
 
+// K-contiguous fragment reads with the 16x16 MFMAs of one chunk per lane
+// and step: lane group g = lane / 16 reads chunk kc_group16(g) of the step
+// (0, 2, 1, 3) instead of chunk g.  A and B take the same order, so each
+// lane still pairs A's and B's values of the same k.  In the natural order
+// these reads measured two-way bank conflicts (the conflict counter at half
+// the LDS-active cycles) while the 32x32 reads measured none; the
+// permutation gives lane groups g and g + 2, which read the same rows, chunks
+// of opposite parity, so those rows' reads fall in different halves of the
+// banks.
+LIBGEMM_HD inline int kc_group16(int g) { return ((g & 1) << 1) | (g >> 1); }
+
 // R-contiguous tile (row-major B or column-major A kept as stored): k-row k
 // holds R values as R/8 chunks; chunk c of k-row k sits at slot
 // c ^ swz_rc(k, mf).  The transposed operand reads (ds_read_b64_tr_b16) of

@@ -965,21 +965,23 @@ __device__ __forceinline__ void k_loop(const Params &p, int m0, int n0, int kbeg
 
     // Per-lane LDS byte offsets of each fragment at step 0; step s XORs in
     // s*KCH chunks (the chunk bits of s and of the lane never overlap).
-    // Lane l holds chunks (l / MF) * FC + c, c < FC, of each step; with
-    // FC = 2 the first of them is even, so chunk c sits at offset ^ 16*c.
+    // Lane l holds chunks lg * FC + c, c < FC, of each step, lg = l / MF
+    // (16x16 with one chunk: kc_group16(l / 16)); with FC = 2 the first of
+    // them is even, so chunk c sits at offset ^ 16*c.
     static_assert(FC == 1 || FC == 2, "fragment chunks");
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+    const int lg = (MF == 16 && FC == 1) ? kc_group16(lane / MF) : lane / MF;
     uint32_t a_off[TM], b_off[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int r = wm * CF::WTM + i * MF + (lane & (MF - 1));
-        a_off[i] = (uint32_t)(r * CH + (((lane / MF) * FC) ^ swz(r))) * 16u;
+        a_off[i] = (uint32_t)(r * CH + ((lg * FC) ^ swz(r))) * 16u;
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int r = wn * CF::WTN + j * MF + (lane & (MF - 1));
-        b_off[j] = (uint32_t)(r * CH + (((lane / MF) * FC) ^ swz(r))) * 16u;
+        b_off[j] = (uint32_t)(r * CH + ((lg * FC) ^ swz(r))) * 16u;
     }
 
     // With two chunks per fragment (fp8) the double-buffered fragments no
@@ -1336,14 +1338,17 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
     };
 
     // per-lane LDS byte offsets of each fragment at step 0, stage 0 (KC: lane
-    // l holds chunks (l / MF) * FC + c, c < FC, of each step, as in k_loop)
+    // l holds chunks lg * FC + c, c < FC, of each step, as in k_loop; the
+    // 16x16 order of kc_group16 only when both operands are read K-contiguous,
+    // as the transposed reads take lane group g to k-group g)
+    const int lg = (MF == 16 && FC == 1 && A_KC && B_KCL) ? kc_group16(lane / MF) : lane / MF;
     uint32_t a_off[TM], b_off[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int rb0 = wm * CF::WTM + i * MF;
         if constexpr (A_KC) {
             const int r = rb0 + (lane & (MF - 1));
-            a_off[i] = (uint32_t)(r * DA::CH + (((lane / MF) * FC) ^ swz_kc(r))) * 16u;
+            a_off[i] = (uint32_t)(r * DA::CH + ((lg * FC) ^ swz_kc(r))) * 16u;
         } else {
             a_off[i] = ES == 2 ? (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BM * 2)
                                : (uint32_t)tr8_read_offset(lane, FC, 0, CF::KSTEP, 0, 0, rb0, BM);
@@ -1354,7 +1359,7 @@ __device__ __forceinline__ void dma_k_loop(const Params &p, int m0, int n0, int 
         const int rb0 = wn * CF::WTN + j * MF;
         if constexpr (B_KCL) {
             const int r = rb0 + (lane & (MF - 1));
-            b_off[j] = (uint32_t)(r * DB::CH + (((lane / MF) * FC) ^ swz_kc(r))) * 16u;
+            b_off[j] = (uint32_t)(r * DB::CH + ((lg * FC) ^ swz_kc(r))) * 16u;
         } else {
             b_off[j] = ES == 2 ? (uint32_t)tr_read_offset(lane, MF, 0, 0, rb0, BN * 2)
                                : (uint32_t)tr8_read_offset(lane, FC, 0, CF::KSTEP, 0, 0, rb0, BN);

@@ -202,7 +202,9 @@ static void check_rc8(int ROWS, int BK, int THREADS, int R, int K, int64_t ld, i
 // operand layout.
 static uint16_t code(int r, int k) { return (uint16_t)(((r & 0x3ff) << 6) ^ (k * 40503u)); }
 
-static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves) {
+// perm: K-contiguous 16x16 reads in the kc_group16 order (both operands
+// K-contiguous), lane group g then holding k-group kc_group16(g)
+static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves, bool perm = false) {
     const int bytes = ROWS * BK * 2, chunks = bytes / 16;
     const int ni = bytes / 1024 / nwaves;
     if (bytes % (1024 * nwaves)) { fail("dma blocks", ROWS, BK, nwaves, 0); return; }
@@ -228,7 +230,8 @@ static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves) {
                 const int kch = kstep * 2 / 16;
                 for (int lane = 0; lane < 64; ++lane) {
                     const int r = rb + lane % MF;
-                    const uint32_t off = (uint32_t)(r * (BK / 8) + ((lane / MF) ^ swz_kc(r))) * 16u;
+                    const int lg = perm ? kc_group16(lane / MF) : lane / MF;
+                    const uint32_t off = (uint32_t)(r * (BK / 8) + (lg ^ swz_kc(r))) * 16u;
                     const uint32_t a = off ^ (uint32_t)(ks * kch * 16);
                     for (int e = 0; e < 8; ++e) got[lane][e] = lds[a / 2 + e];
                 }
@@ -249,7 +252,8 @@ static void check_dma_tile(int ROWS, int BK, int MF, bool KC, int nwaves) {
             }
             for (int lane = 0; lane < 64; ++lane)
                 for (int e = 0; e < 8; ++e) {
-                    const int r = rb + lane % MF, k = ks * kstep + 8 * (lane / MF) + e;
+                    const int lg = perm ? kc_group16(lane / MF) : lane / MF;
+                    const int r = rb + lane % MF, k = ks * kstep + 8 * lg + e;
                     ++g_checked;
                     if (got[lane][e] != code(r, k)) fail("fragment value", lane, e, r, k);
                 }
@@ -437,6 +441,18 @@ int main() {
     for (int nw : {4, 8})
         for (int mf : {32, 16})
             for (bool kc : {true, false}) check_dma_tile(256, 64, mf, kc, nw);
+    for (int nw : {4, 8}) check_dma_tile(256, 64, 16, true, nw, true);
+    // the 16x16 lane-group order: a permutation, groups g and g + 2 (which
+    // read the same rows) at chunks of opposite parity
+    {
+        int seen = 0;
+        for (int g = 0; g < 4; ++g) {
+            seen |= 1 << kc_group16(g);
+            ++g_checked;
+            if (g < 2 && ((kc_group16(g) ^ kc_group16(g + 2)) & 1) != 1) fail("kc_group16 parity", g, 0, 0, 0);
+        }
+        if (seen != 15) fail("kc_group16 permutation", seen, 0, 0, 0);
+    }
     // the DMA loads' global offsets over the problem sides above (16-byte
     // lines as the DMA entries require), 16-bit and 8-bit, both orders, the
     // plain and the clamped form
