@@ -143,10 +143,12 @@ typedef enum {
  * row-major (and, for gemm_run_ex, a per-column bias is 16-byte aligned);
  * otherwise element by element.
  *
- * fp8 accuracy: gfx950's fp8 MFMA adds each block of 64 products (per
- * output) with a relative precision of about 2^-14 of the block's largest
- * product (measured), before the fp32 accumulation; products of inputs of
- * similar magnitude, and integer-valued inputs, come out exact.
+ * fp8 accuracy: gfx950's fp8 MFMA adds the products of each output in
+ * groups of 8 consecutive k, aligned to the largest product of the group:
+ * what lies below 2^-13 of that product is lost (measured, E4M3 and E5M2),
+ * before the fp32 accumulation.  Each product is then off by less than
+ * 2^-13 * max|a| * max|b|.  Products of inputs of similar magnitude, and
+ * integer-valued inputs, come out exact.
  */
 int gemm_run(int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda, int layoutA,
