@@ -171,6 +171,31 @@ def _entry_shapes():
     return out
 
 
+@pytest.mark.parametrize("K", [64, 256])
+def test_f16_products_far_below_the_largest_are_kept(K):
+    """Unlike the fp8 MFMA (test_fp8_gpu.test_fp8_group_truncation), the
+    16-bit MFMAs keep products far below the largest one: A holds 2^8 at
+    every k % 64 == 0 and 2^(8-r) elsewhere, B holds 2^8, so each row sums
+    one product 2^16 and 63 products 2^(16-r) per 64 k; for r up to 22 the
+    sum is representable in fp32, and every 16-bit entry returns it exactly."""
+    M, N = 64, 64
+    for r in (14, 18, 22):
+        prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="int",
+                              seed=9950)
+        a = np.full((M, K), 2.0 ** (8 - r), dtype=np.float16)
+        a[:, 0:K:64] = 256.0
+        prob.A[:, :K] = a.view(np.uint16)
+        prob.B[:, :K] = np.float16(256.0).view(np.uint16)
+        exact = (K // 64) * (2.0 ** 16 + 63 * 2.0 ** (16 - r))
+        assert np.all(region(prob, oracle_full(prob)).astype(np.float64) == exact)
+        for cid in sorted(ENTRY_TILE):
+            log("case: f16 small products r %d K %d config %d" % (r, K, cid))
+            dp = DeviceProblem(prob)
+            dp.run(config=cid)
+            got = region(prob, dp.result()).astype(np.float64)
+            assert np.all(got == exact), (cid, r, got.ravel()[:4], exact)
+
+
 def test_config_ids_match_table():
     # 16-bit entries here; the int8 entries (ids 5..8, 17, 19) and the fp8
     # entries (ids 9..12, 18) are covered by test_int8_gpu and test_fp8_gpu
