@@ -171,8 +171,16 @@ def _entry_shapes():
     return out
 
 
+def _bits16(x: np.ndarray, in_dtype: int) -> np.ndarray:
+    """fp16 or bf16 bit patterns of values exact in both formats."""
+    if in_dtype == F16:
+        return x.astype(np.float16).view(np.uint16)
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("in_dtype", [F16, BF16])
 @pytest.mark.parametrize("K", [64, 256])
-def test_f16_products_far_below_the_largest_are_kept(K):
+def test_f16_products_far_below_the_largest_are_kept(K, in_dtype):
     """Unlike the fp8 MFMA (test_fp8_gpu.test_fp8_group_truncation), the
     16-bit MFMAs keep products far below the largest one: A holds 2^8 at
     every k % 64 == 0 and 2^(8-r) elsewhere, B holds 2^8, so each row sums
@@ -181,15 +189,15 @@ def test_f16_products_far_below_the_largest_are_kept(K):
     M, N = 64, 64
     for r in (14, 18, 22):
         prob = W.make_problem(M, N, K, layoutA=ROW_MAJOR, layoutB=COL_MAJOR, values="int",
-                              seed=9950)
-        a = np.full((M, K), 2.0 ** (8 - r), dtype=np.float16)
+                              in_dtype=in_dtype, seed=9950)
+        a = np.full((M, K), 2.0 ** (8 - r))
         a[:, 0:K:64] = 256.0
-        prob.A[:, :K] = a.view(np.uint16)
-        prob.B[:, :K] = np.float16(256.0).view(np.uint16)
+        prob.A[:, :K] = _bits16(a, in_dtype)
+        prob.B[:, :K] = _bits16(np.full((N, K), 256.0), in_dtype)
         exact = (K // 64) * (2.0 ** 16 + 63 * 2.0 ** (16 - r))
         assert np.all(region(prob, oracle_full(prob)).astype(np.float64) == exact)
         for cid in sorted(ENTRY_TILE):
-            log("case: f16 small products r %d K %d config %d" % (r, K, cid))
+            log("case: 16-bit small products dtype %d r %d K %d config %d" % (in_dtype, r, K, cid))
             dp = DeviceProblem(prob)
             dp.run(config=cid)
             got = region(prob, dp.result()).astype(np.float64)
